@@ -1,0 +1,251 @@
+"""Plain CPU oracle for one sequence-parallel rank's share of block-sparse attention (fp64, NumPy).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+or call this module.  The product path (the HIP library and its Python binding) never does: it shares
+no code, header, table or helper with this file, and this file imports nothing from it.
+
+Source: "SparSP: Exploiting Communication Sparsity for Sequence-Parallel Video DiTs" (the paper's full
+text as published on paperpeel.com).  What it computes, step by step:
+
+1. The rank's local query blocks Q_r = {i : P(i) = r} (section 4.1, Eq. 2 uses Q_r; section 4.3 fixes P
+   once per geometry).
+2. The per-head demand union U[h] = {j : exists i in Q_r with M[h, i, j] = 1} (Eq. 2, taken over all
+   owners p at once; section 5.2 "head-preserving demand": never unioned across heads).
+3. The per-peer compaction: for p = 0..G-1, then h = 0..H-1, then ascending j with j in U[h] and
+   P(j) = p, the next packed slot (section 5.2 "metadata-free exchange": one (head, block) enumeration
+   in row-major order that both ends derive, each head a contiguous range; section 6.1: one slot region
+   per peer).  Segment offsets are exclusive prefix sums of the (p, h) counts.
+4. The pack: slot s holds K[h_s] rows of block j_s (b x d, token-major) followed by V[h_s] rows of block
+   j_s stored transposed (d x b, key-contiguous), both bfloat16 bit patterns.  The pages say the
+   selected blocks are packed contiguously and then laid out for the attention kernel on arrival
+   (section 6.2); the transposed V is that layout, written at pack time.
+5. Block-sparse attention: for each head and local query block, softmax(Q K^T / sqrt(d)) V over exactly
+   the key tokens of the blocks the mask row selects (section 2.2 gives the dense formula; Eq. 2's block
+   mask M restricts it).  Key tokens at index >= N (the zero padding of the last block) are excluded.
+   An empty key set gives O = 0 and lse = -inf.  lse = m + ln(sum exp(s - m)) is the natural-log
+   log-sum-exp that an online-softmax merge across pieces of KV needs (section 2.3).
+
+Everything is fp64 on the exact values of the bfloat16 inputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# --------------------------------------------------------------------------------------------------
+# data format
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) -> float64: a bfloat16 is the high half of an IEEE float32."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+# --------------------------------------------------------------------------------------------------
+# step 1: the local set
+
+
+def local_query_blocks(placement: np.ndarray, r: int) -> np.ndarray:
+    """Q_r as an ascending int32 array: every logical block i with P(i) = r (section 4.1, Eq. 2)."""
+    return np.array([i for i, p in enumerate(np.asarray(placement).tolist()) if p == r], dtype=np.int32)
+
+
+# --------------------------------------------------------------------------------------------------
+# step 2: demand union (Eq. 2, per head)
+
+
+def demand_union_sets(mask: np.ndarray, nb: int) -> list[set]:
+    """Brute force: U[h] as a Python set, built entry by entry (small inputs only)."""
+    H, Lq = mask.shape[0], mask.shape[1]
+    out = []
+    for h in range(H):
+        u = set()
+        for k in range(Lq):
+            for j in range(nb):
+                if mask[h, k, j]:
+                    u.add(j)
+        out.append(u)
+    return out
+
+
+def demand_union(mask: np.ndarray, nb: int) -> np.ndarray:
+    """U[h][j] = OR over the rank's rows k of M[h, k, j]; bool [H][nb]."""
+    m = np.asarray(mask)[:, :, :nb] != 0
+    if m.shape[1] == 0:
+        return np.zeros((m.shape[0], nb), dtype=bool)
+    return np.any(m, axis=1)
+
+
+def demand_words(U: np.ndarray) -> np.ndarray:
+    """Bit-pack U into uint64 words: bit (j mod 64) of word floor(j/64); bits past nb are 0."""
+    H, nb = U.shape
+    W = -(-nb // 64)
+    words = np.zeros((H, W), dtype=np.uint64)
+    for h in range(H):
+        for j in np.flatnonzero(U[h]):
+            words[h, j // 64] |= np.uint64(1) << np.uint64(j % 64)
+    return words
+
+
+# --------------------------------------------------------------------------------------------------
+# step 3: per-peer compaction (section 5.2)
+
+
+def compact(U: np.ndarray, placement: np.ndarray, G: int) -> dict:
+    """Enumerate (p, h, j) in row-major order and number the demanded blocks.
+
+    Returns seg_offsets int32 [G*H+1] (index p*H + h; the last entry is S), slot_block and slot_head
+    int32 [S], slot_of int32 [H][nb] (-1 where not demanded) and S.
+    """
+    H, nb = U.shape
+    P = np.asarray(placement)
+    counts = np.zeros(G * H, dtype=np.int64)
+    blocks, heads = [], []
+    for p in range(G):
+        owned = P == p
+        for h in range(H):
+            js = np.flatnonzero(U[h] & owned)          # ascending
+            counts[p * H + h] = len(js)
+            blocks.append(js)
+            heads.append(np.full(len(js), h))
+    seg = np.zeros(G * H + 1, dtype=np.int64)
+    seg[1:] = np.cumsum(counts)
+    slot_block = np.concatenate(blocks).astype(np.int32) if blocks else np.zeros(0, np.int32)
+    slot_head = np.concatenate(heads).astype(np.int32) if heads else np.zeros(0, np.int32)
+    slot_of = np.full((H, nb), -1, dtype=np.int32)
+    slot_of[slot_head, slot_block] = np.arange(len(slot_block), dtype=np.int32)
+    return dict(seg_offsets=seg.astype(np.int32), slot_block=slot_block, slot_head=slot_head,
+                slot_of=slot_of, S=int(seg[-1]))
+
+
+def compact_bruteforce(U_sets: list[set], placement, G: int, nb: int) -> dict:
+    """The same enumeration with Python loops and a running counter (small inputs only)."""
+    H = len(U_sets)
+    seg, slot_block, slot_head = [], [], []
+    slot_of = [[-1] * nb for _ in range(H)]
+    s = 0
+    for p in range(G):
+        for h in range(H):
+            seg.append(s)
+            for j in range(nb):
+                if j in U_sets[h] and int(placement[j]) == p:
+                    slot_block.append(j)
+                    slot_head.append(h)
+                    slot_of[h][j] = s
+                    s += 1
+    seg.append(s)
+    return dict(seg_offsets=np.array(seg, np.int32), slot_block=np.array(slot_block, np.int32),
+                slot_head=np.array(slot_head, np.int32), slot_of=np.array(slot_of, np.int32), S=s)
+
+
+def segment_range(seg_offsets: np.ndarray, H: int, p: int) -> tuple[int, int]:
+    """Slots [lo, hi) of source rank p: its heads are consecutive (section 6.2, derived byte ranges)."""
+    return int(seg_offsets[p * H]), int(seg_offsets[(p + 1) * H])
+
+
+# --------------------------------------------------------------------------------------------------
+# step 4: pack
+
+
+def pack(K: np.ndarray, V: np.ndarray, slot_block: np.ndarray, slot_head: np.ndarray, b: int) -> np.ndarray:
+    """packed[s, 0] = K[h_s, j_s*b:(j_s+1)*b, :] (b x d); packed[s, 1] = that V block transposed (d x b).
+
+    Bit patterns in, bit patterns out (uint16 [S][2][b*d]).
+    """
+    S = len(slot_block)
+    d = K.shape[2]
+    out = np.empty((S, 2, b * d), dtype=np.uint16)
+    for s in range(S):
+        h, j = int(slot_head[s]), int(slot_block[s])
+        out[s, 0] = K[h, j * b:(j + 1) * b, :].reshape(-1)
+        out[s, 1] = V[h, j * b:(j + 1) * b, :].T.reshape(-1)
+    return out
+
+
+# --------------------------------------------------------------------------------------------------
+# step 5: block-sparse attention
+
+
+def _attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
+    """Exact softmax attention of query rows q over key rows k (fp64).  Returns (O, lse, weights)."""
+    if k.shape[0] == 0:
+        return (np.zeros((q.shape[0], v.shape[1])), np.full(q.shape[0], -np.inf),
+                np.zeros((q.shape[0], 0)))
+    s = (q @ k.T) * scale
+    m = s.max(axis=1, keepdims=True)
+    e = np.exp(s - m)
+    l = e.sum(axis=1, keepdims=True)
+    w = e / l
+    return w @ v, (m + np.log(l))[:, 0], w
+
+
+def allowed_keys(mask_row: np.ndarray, nb: int, b: int, N: int) -> np.ndarray:
+    """Token indices a query block may attend to: the real tokens of every selected key block."""
+    js = np.flatnonzero(np.asarray(mask_row)[:nb])
+    if len(js) == 0:
+        return np.zeros(0, dtype=np.int64)
+    toks = (js[:, None] * b + np.arange(b)[None, :]).reshape(-1)
+    return toks[toks < N]
+
+
+def attention_block(Q, K, V, mask, h: int, k: int, b: int, N: int, scale: float):
+    """O (b x d) and lse (b) for local query block k of head h."""
+    nb = -(-N // b)
+    toks = allowed_keys(mask[h, k], nb, b, N)
+    q = bf16_to_f64(Q[h, k * b:(k + 1) * b])
+    kk = bf16_to_f64(K[h, toks])
+    vv = bf16_to_f64(V[h, toks])
+    O, lse, _ = _attend(q, kk, vv, scale)
+    return O, lse
+
+
+def attention(Q, K, V, mask, b: int, N: int, scale: float, items=None):
+    """Block-sparse attention for the rank's local queries.
+
+    Q uint16 [H][Lq*b][d]; K, V uint16 [H][nb*b][d]; mask uint8 [H][Lq][>= nb].
+    Returns O float64 [H][Lq*b][d] and lse float64 [H][Lq*b].  With ``items`` (a list of (h, k)) only
+    those query blocks are computed; the others stay NaN.
+    """
+    H, Lq = mask.shape[0], mask.shape[1]
+    d = Q.shape[2]
+    O = np.full((H, Lq * b, d), np.nan)
+    lse = np.full((H, Lq * b), np.nan)
+    todo = items if items is not None else [(h, k) for h in range(H) for k in range(Lq)]
+    for h, k in todo:
+        O[h, k * b:(k + 1) * b], lse[h, k * b:(k + 1) * b] = attention_block(Q, K, V, mask, h, k, b, N, scale)
+    return O, lse
+
+
+def token_mask(mask_rows: np.ndarray, q_blocks: np.ndarray, b: int, N: int) -> np.ndarray:
+    """Expand one head's block mask rows [Lq][nb] to a token mask [Lq*b][nb*b]: M kron ones(b, b),
+    with key tokens >= N switched off."""
+    nb = -(-N // b)
+    m = np.kron(np.asarray(mask_rows)[:, :nb] != 0, np.ones((b, b), dtype=bool))
+    m[:, N:] = False
+    return m
+
+
+def dense_masked_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, tmask: np.ndarray, scale: float):
+    """The dense formula of section 2.2 with disallowed logits set to -inf (self-check only).
+
+    q [n][d], k and v [m][d] float64; tmask bool [n][m].  Returns (O, lse, weights)."""
+    s = (q @ k.T) * scale
+    s = np.where(tmask, s, -np.inf)
+    m = s.max(axis=1, keepdims=True)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.exp(s - m_safe)
+    l = e.sum(axis=1, keepdims=True)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        w = np.where(l > 0, e / np.where(l > 0, l, 1.0), 0.0)
+        lse = np.where(l[:, 0] > 0, m_safe[:, 0] + np.log(np.where(l[:, 0] > 0, l[:, 0], 1.0)), -np.inf)
+    return w @ v, lse, w
+
+
+# --------------------------------------------------------------------------------------------------
+# comparison helpers (used by the tests and the benchmark's CPU leg)
+
+
+def real_rows(q_blocks: np.ndarray, b: int, N: int) -> np.ndarray:
+    """Boolean [Lq*b]: which local query rows are real tokens (< N)."""
+    tok = (np.asarray(q_blocks, dtype=np.int64)[:, None] * b + np.arange(b)[None, :]).reshape(-1)
+    return tok < N
