@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark one sequence-parallel rank's share of block-sparse attention on one MI355X.
+
+A step is one pass of the whole hot path over one synthetic workload already resident in HBM:
+demand union + compaction (sparsp_demand_union), the K/V pack (sparsp_pack_kv) and block-sparse
+attention (sparsp_block_sparse_attn), all enqueued on torch's current stream.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config hunyuan] [--no-cpu]
+
+Prints one JSON line.  ``value`` is the effective attention throughput of the whole step: the
+algorithmic FLOPs of the selected tiles (4*b*b*d per selected (head, query block, key block)) divided by
+the step time.  Per-kernel durations come from HIP events recorded on the launch stream around every
+call in the timed steps.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "block-sparse attn effective TFLOP/s + KV pack GB/s, one rank's share"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="hunyuan")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle attention sample")
+    return ap.parse_args()
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_attention_rank_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it matches these sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("sources_digest") != kernel_sources_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s: float, pairs: int, attn_flops: float):
+    """Time the CPU oracle: union + compaction + pack on the whole workload, attention on as many
+    (head, query block) items as fit in the budget; extrapolate the attention to all items."""
+    import numpy as np
+    import oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    w = inp["workload"]
+    t0 = time.perf_counter()
+    U = O.demand_union(inp["mask"], w.nb)
+    c = O.compact(U, inp["placement"], w.G)
+    t_union = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.pack(inp["K"], inp["V"], c["slot_block"], c["slot_head"], w.b)
+    t_pack = time.perf_counter() - t0
+    H, Lq = w.H, len(inp["q_blocks"])
+    rng = np.random.default_rng(0)
+    order = rng.permutation(H * Lq)
+    scale = 1.0 / math.sqrt(w.d)
+    done_pairs, n_items, t_attn = 0, 0, 0.0
+    for idx in order:
+        h, k = divmod(int(idx), Lq)
+        t0 = time.perf_counter()
+        O.attention_block(inp["Q"], inp["K"], inp["V"], inp["mask"], h, k, w.b, w.N, scale)
+        t_attn += time.perf_counter() - t0
+        done_pairs += int(inp["mask"][h, k, :w.nb].sum())
+        n_items += 1
+        if t_attn >= budget_s:
+            break
+    t_attn_full = t_attn * pairs / max(done_pairs, 1)
+    t_step = t_union + t_pack + t_attn_full
+    return {
+        "value": attn_flops / t_step / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle on {w.name}: union+compaction and pack on the whole workload "
+                   f"({t_union:.2f} s, {t_pack:.2f} s); attention on {n_items} of {H * Lq} (head, query block) "
+                   f"items ({done_pairs} of {pairs} tiles, {t_attn:.1f} s), extrapolated by tile count to "
+                   f"{t_attn_full:.0f} s; value = all tiles' FLOPs / ({t_union:.2f} + {t_pack:.2f} + "
+                   f"{t_attn_full:.0f}) s"),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share only; --gpus {args.gpus} is not supported (use --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import block_sparse_attention_rank_amd as bsa
+    from workloads import CONFIGS, make_inputs
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = CONFIGS[args.config]
+    t0 = time.perf_counter()
+    inp = make_inputs(w)
+    print(f"[bench] inputs for {w.name} drawn in {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    Lq = len(inp["q_blocks"])
+    g = bsa.geometry(H=w.H, d=w.d, b=w.b, N=w.N, G=w.G, r=w.r, Lq=Lq)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    mask = torch.from_numpy(inp["mask"]).cuda()
+    placement = torch.from_numpy(inp["placement"]).cuda()
+    Q, K, V = bf16(inp["Q"]), bf16(inp["K"]), bf16(inp["V"])
+    u = bsa.empty_union(g)
+    packed = torch.empty((g.H * g.nb, 2, g.b * g.d), dtype=torch.bfloat16, device="cuda")
+    O = torch.empty((g.H, Lq * g.b, g.d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((g.H, Lq * g.b), dtype=torch.float32, device="cuda")
+    scale = 1.0 / math.sqrt(g.d)
+    stream = torch.cuda.current_stream()
+
+    pairs = int(inp["mask"][:, :, :w.nb].astype(np.int64).sum())
+    attn_flops = 4.0 * g.b * g.b * g.d * pairs
+    mask_bytes = int(inp["mask"].size)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        bsa.demand_union(g, mask, placement, out=u)
+        if ev is not None:
+            ev[1].record(stream)
+        bsa.pack_kv(g, K, V, u, out=packed)
+        if ev is not None:
+            ev[2].record(stream)
+        bsa.block_sparse_attn(g, Q, mask, u.slot_of, packed, scale, out=(O, lse))
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    S = int(u.seg_offsets[-1].item())
+    seg = u.seg_offsets.cpu().numpy()
+    own_lo, own_hi = int(seg[w.r * g.H]), int(seg[(w.r + 1) * g.H])
+    slot_bytes = 2 * g.b * g.d * 2
+    pack_bytes = 2 * S * slot_bytes            # read + write
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = lambda a, b: float(np.mean([e[a].elapsed_time(e[b]) for e in events]))  # noqa: E731
+    t_union, t_pack, t_attn = ms(0, 1), ms(1, 2), ms(2, 3)
+    ms_per_step = wall * 1e3 / args.steps
+    print(f"[bench] {w.name}: union {t_union * 1e3:.1f} us, pack {t_pack * 1e3:.1f} us, "
+          f"attention {t_attn:.3f} ms, step {ms_per_step:.3f} ms", file=sys.stderr, flush=True)
+
+    attn_tflops = attn_flops / (t_attn * 1e-3) / 1e12
+    pack_gbs = pack_bytes / (t_pack * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(attn_flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: {w.note}",
+            "H": g.H, "d": g.d, "b": g.b, "N": g.N, "nb": g.nb, "G": g.G, "r": g.r, "Lq": Lq,
+            "placement": w.placement, "selected_tiles": pairs,
+            "density": round(pairs / (g.H * Lq * g.nb), 4),
+            "slots_S": S, "wire_slots": S - (own_hi - own_lo), "wire_bytes": (S - (own_hi - own_lo)) * slot_bytes,
+        },
+        "components": {
+            "union_compact_us": round(t_union * 1e3, 2),
+            "union_mask_GBps": round(mask_bytes / (t_union * 1e-3) / 1e9, 1),
+            "pack_us": round(t_pack * 1e3, 2),
+            "pack_GBps": round(pack_gbs, 1),
+            "pack_frac_hbm": round(pack_gbs / HBM_PEAK_GBS, 4),
+            "attn_ms": round(t_attn, 4),
+            "attn_TFLOPs": round(attn_tflops, 2),
+            "attn_frac_bf16": round(attn_tflops / BF16_DENSE_TFLOPS, 4),
+        },
+        "roofline": {
+            "kernel": "bsa_fwd_kernel",
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 2),
+            "peak": BF16_DENSE_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / BF16_DENSE_TFLOPS, 4),
+            "traffic": measured_traffic("bsa_fwd", w.name),
+        },
+        "roofline_pack": {
+            "kernel": "pack_kernel",
+            "bound": "hbm",
+            "achieved": round(pack_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(pack_gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("pack", w.name),
+        },
+        "sources_digest": kernel_sources_digest(),
+    }
+    if not args.no_cpu:
+        t0 = time.perf_counter()
+        rec["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds, pairs, attn_flops)
+        print(f"[bench] cpu baseline took {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

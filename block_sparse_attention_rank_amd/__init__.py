@@ -1,0 +1,135 @@
+"""One sequence-parallel rank's share of block-sparse attention on MI355X (gfx950).
+
+A thin binding over the C ABI of ``libsparsp.so`` (include/sparsp.h): torch tensors are used for device
+memory and streams only, every step of the path runs in the library's HIP kernels.  The calls follow
+"SparSP: Exploiting Communication Sparsity for Sequence-Parallel Video DiTs": the per-head demand union of
+Eq. 2 and its compaction (sections 4.1 and 5.2), the demand-directed pack of K/V (sections 5.1, 6.1 and
+6.2) and block-sparse attention with an online softmax (sections 2.2 and 2.3).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+from ._lib import EXPORTS, LIB_PATH, Geometry, SparspError, check, load  # noqa: F401
+
+__all__ = ["Geometry", "SparspError", "UnionResult", "geometry", "local_query_blocks", "demand_union",
+           "pack_kv", "block_sparse_attn", "load", "LIB_PATH", "EXPORTS"]
+
+
+def geometry(H: int, d: int, b: int, N: int, G: int, r: int, Lq: int) -> Geometry:
+    return Geometry(H, d, b, N, G, r, Lq)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _require(t, name, dtype, shape=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def local_query_blocks(placement: np.ndarray, G: int, r: int) -> np.ndarray:
+    """Q_r = {i : P(i) = r}, ascending (host call)."""
+    P = np.ascontiguousarray(placement, dtype=np.int32)
+    out = np.empty(len(P), dtype=np.int32)
+    n = ctypes.c_int32(0)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    check(load().sparsp_local_query_blocks(P.ctypes.data_as(i32p), len(P), G, r, out.ctypes.data_as(i32p),
+                                           len(out), ctypes.byref(n)))
+    return out[:n.value].copy()
+
+
+@dataclass
+class UnionResult:
+    demand: "torch.Tensor"        # int64 view of uint64 words [H][W]
+    seg_offsets: "torch.Tensor"   # int32 [G*H + 1]
+    slot_block: "torch.Tensor"    # int32 [H*nb]
+    slot_head: "torch.Tensor"     # int32 [H*nb]
+    slot_of: "torch.Tensor"       # int32 [H][nb]
+
+
+def empty_union(g: Geometry, device="cuda") -> UnionResult:
+    import torch
+    nb, W = g.nb, g.W
+    return UnionResult(
+        demand=torch.empty((g.H, W), dtype=torch.int64, device=device),
+        seg_offsets=torch.empty(g.G * g.H + 1, dtype=torch.int32, device=device),
+        slot_block=torch.empty(g.H * nb, dtype=torch.int32, device=device),
+        slot_head=torch.empty(g.H * nb, dtype=torch.int32, device=device),
+        slot_of=torch.empty((g.H, nb), dtype=torch.int32, device=device),
+    )
+
+
+def demand_union(g: Geometry, mask, placement, out: UnionResult | None = None, stream=None) -> UnionResult:
+    """Per-head demand union and per-peer compaction (sparsp_demand_union)."""
+    import torch
+    _require(mask, "mask", torch.uint8)
+    _require(placement, "placement", torch.int32, (g.nb,))
+    if mask.dim() != 3 or mask.shape[0] != g.H or mask.shape[1] != g.Lq:
+        raise ValueError("mask must be [H][Lq][pitch]")
+    out = out or empty_union(g, mask.device)
+    check(load().sparsp_demand_union(ctypes.byref(g), _ptr(mask), mask.shape[2], _ptr(placement), _ptr(out.demand),
+                                     _ptr(out.seg_offsets), _ptr(out.slot_block), _ptr(out.slot_head),
+                                     _ptr(out.slot_of), _stream(stream)))
+    return out
+
+
+def pack_kv(g: Geometry, K, V, u: UnionResult, slot_capacity: int | None = None, out=None, stream=None):
+    """Gather the demanded K/V blocks into the compacted buffer (sparsp_pack_kv).
+
+    Returns ``packed`` as a bfloat16 tensor [slot_capacity][2][b*d]; the default capacity is H*nb."""
+    import torch
+    shape = (g.H, g.nb * g.b, g.d)
+    _require(K, "K", torch.bfloat16, shape)
+    _require(V, "V", torch.bfloat16, shape)
+    cap = slot_capacity if slot_capacity is not None else g.H * g.nb
+    if out is None:
+        out = torch.empty((cap, 2, g.b * g.d), dtype=torch.bfloat16, device=K.device)
+    else:
+        _require(out, "packed", torch.bfloat16)
+        cap = out.shape[0]
+    check(load().sparsp_pack_kv(ctypes.byref(g), _ptr(K), _ptr(V), _ptr(u.seg_offsets), _ptr(u.slot_block),
+                                _ptr(u.slot_head), cap, _ptr(out), _stream(stream)))
+    return out
+
+
+def block_sparse_attn(g: Geometry, Q, mask, slot_of, packed, softmax_scale: float | None = None,
+                      out=None, stream=None):
+    """Block-sparse flash attention over the compacted K/V (sparsp_block_sparse_attn).
+
+    Returns (O float32 [H][Lq*b][d], lse float32 [H][Lq*b])."""
+    import torch
+    _require(Q, "Q", torch.bfloat16, (g.H, g.Lq * g.b, g.d))
+    _require(mask, "mask", torch.uint8)
+    _require(slot_of, "slot_of", torch.int32, (g.H, g.nb))
+    _require(packed, "packed", torch.bfloat16)
+    scale = 1.0 / math.sqrt(g.d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        O = torch.empty((g.H, g.Lq * g.b, g.d), dtype=torch.float32, device=Q.device)
+        lse = torch.empty((g.H, g.Lq * g.b), dtype=torch.float32, device=Q.device)
+    else:
+        O, lse = out
+    check(load().sparsp_block_sparse_attn(ctypes.byref(g), _ptr(Q), _ptr(mask), mask.shape[2], _ptr(slot_of),
+                                          _ptr(packed), packed.shape[0], scale, _ptr(O), _ptr(lse),
+                                          _stream(stream)))
+    return O, lse

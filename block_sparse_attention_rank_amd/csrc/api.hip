@@ -1,0 +1,155 @@
+// The C ABI of libsparsp: argument checks, geometry derivation and kernel launches.  Declarations and the
+// contract of every entry point are in include/sparsp.h.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/sparsp.h"
+#include "sparsp_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t status, const char* fn, const char* what) {
+  char buf[512];
+  snprintf(buf, sizeof(buf), "%s: %s", fn, what);
+  g_last_error = buf;
+  return status;
+}
+
+int32_t hip_status(hipError_t e, const char* fn) {
+  if (e == hipSuccess) return SPARSP_OK;
+  char buf[512];
+  snprintf(buf, sizeof(buf), "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+  g_last_error = buf;
+  return SPARSP_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates the geometry shared by every device call; fills `out` on success.
+int32_t check_geometry(const sparsp_geometry* g, const char* fn, sparsp::Dims* out) {
+  if (!g) return fail(SPARSP_ERR_INVALID, fn, "geometry is NULL");
+  if (g->H < 1) return fail(SPARSP_ERR_INVALID, fn, "H must be >= 1");
+  if (g->N < 1) return fail(SPARSP_ERR_INVALID, fn, "N must be >= 1");
+  if (g->G < 1) return fail(SPARSP_ERR_INVALID, fn, "G must be >= 1");
+  if (g->r < 0 || g->r >= g->G) return fail(SPARSP_ERR_INVALID, fn, "r must lie in [0, G)");
+  if (g->d != 64 && g->d != 128) return fail(SPARSP_ERR_UNSUPPORTED, fn, "d must be 64 or 128");
+  if (g->b != 64 && g->b != 128) return fail(SPARSP_ERR_UNSUPPORTED, fn, "b must be 64 or 128");
+  if (g->G > sparsp::kMaxRanks) return fail(SPARSP_ERR_UNSUPPORTED, fn, "G must be <= 64");
+  const int64_t nb = ((int64_t)g->N + g->b - 1) / g->b;
+  if (nb > sparsp::kMaxBlocks) return fail(SPARSP_ERR_UNSUPPORTED, fn, "nb = ceil(N/b) must be <= 16384");
+  if (g->Lq < 0 || g->Lq > nb) return fail(SPARSP_ERR_INVALID, fn, "Lq must lie in [0, nb]");
+  if ((int64_t)g->H * nb > (1ll << 30)) return fail(SPARSP_ERR_UNSUPPORTED, fn, "H*nb must be <= 2^30");
+  out->H = g->H;
+  out->d = g->d;
+  out->b = g->b;
+  out->N = g->N;
+  out->G = g->G;
+  out->r = g->r;
+  out->Lq = g->Lq;
+  out->nb = (int)nb;
+  out->W = (int)((nb + 63) / 64);
+  return SPARSP_OK;
+}
+
+int32_t check_mask(const sparsp::Dims& d, const uint8_t* mask, int64_t pitch, const char* fn) {
+  if (!mask && d.Lq > 0) return fail(SPARSP_ERR_INVALID, fn, "mask is NULL");
+  if (pitch < d.nb || pitch % 16 != 0) return fail(SPARSP_ERR_INVALID, fn, "mask_pitch must be >= nb and a multiple of 16");
+  if (mask && !aligned16(mask)) return fail(SPARSP_ERR_INVALID, fn, "mask must be 16-byte aligned");
+  return SPARSP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sparsp_abi_version(void) { return SPARSP_ABI_VERSION; }
+
+const char* sparsp_status_string(int32_t status) {
+  switch (status) {
+    case SPARSP_OK: return "ok";
+    case SPARSP_ERR_INVALID: return "invalid argument";
+    case SPARSP_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SPARSP_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* sparsp_last_error(void) { return g_last_error.c_str(); }
+
+int32_t sparsp_local_query_blocks(const int32_t* placement, int32_t nb, int32_t G, int32_t r, int32_t* q_blocks,
+                                  int32_t capacity, int32_t* Lq) {
+  static const char* fn = "sparsp_local_query_blocks";
+  if (!placement || !Lq) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
+  if (nb < 1 || G < 1) return fail(SPARSP_ERR_INVALID, fn, "nb and G must be >= 1");
+  if (r < 0 || r >= G) return fail(SPARSP_ERR_INVALID, fn, "r must lie in [0, G)");
+  int32_t n = 0;
+  for (int32_t i = 0; i < nb; ++i) {
+    if (placement[i] < 0 || placement[i] >= G) return fail(SPARSP_ERR_INVALID, fn, "placement value outside [0, G)");
+    n += placement[i] == r;
+  }
+  *Lq = n;
+  if (n > capacity || (n > 0 && !q_blocks)) return fail(SPARSP_ERR_INVALID, fn, "q_blocks capacity too small");
+  int32_t k = 0;
+  for (int32_t i = 0; i < nb; ++i)
+    if (placement[i] == r) q_blocks[k++] = i;
+  return SPARSP_OK;
+}
+
+int32_t sparsp_demand_union(const sparsp_geometry* geom, const uint8_t* mask, int64_t mask_pitch,
+                            const int32_t* placement, uint64_t* demand, int32_t* seg_offsets, int32_t* slot_block,
+                            int32_t* slot_head, int32_t* slot_of, void* stream) {
+  static const char* fn = "sparsp_demand_union";
+  sparsp::Dims d;
+  int32_t st = check_geometry(geom, fn, &d);
+  if (st) return st;
+  if ((st = check_mask(d, mask, mask_pitch, fn))) return st;
+  if (!placement || !demand || !seg_offsets || !slot_block || !slot_head || !slot_of)
+    return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
+  if (sparsp::compact_lds_bytes(d) > (size_t)sparsp::kCompactLdsLimit)
+    return fail(SPARSP_ERR_UNSUPPORTED, fn, "G*W*12 + (G*H+1)*4 exceeds 64 KiB of LDS");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = sparsp::launch_union(d, mask, mask_pitch, demand, s);
+  if (e == hipSuccess) e = sparsp::launch_compact(d, placement, demand, seg_offsets, slot_block, slot_head, slot_of, s);
+  return hip_status(e, fn);
+}
+
+int32_t sparsp_pack_kv(const sparsp_geometry* geom, const uint16_t* K, const uint16_t* V, const int32_t* seg_offsets,
+                       const int32_t* slot_block, const int32_t* slot_head, int32_t slot_capacity, uint16_t* packed,
+                       void* stream) {
+  static const char* fn = "sparsp_pack_kv";
+  sparsp::Dims d;
+  int32_t st = check_geometry(geom, fn, &d);
+  if (st) return st;
+  if (!K || !V || !seg_offsets || !slot_block || !slot_head || !packed) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
+  if (slot_capacity < 1) return fail(SPARSP_ERR_INVALID, fn, "slot_capacity must be >= 1");
+  if (!aligned16(K) || !aligned16(V) || !aligned16(packed))
+    return fail(SPARSP_ERR_INVALID, fn, "K, V and packed must be 16-byte aligned");
+  return hip_status(sparsp::launch_pack(d, K, V, seg_offsets, slot_block, slot_head, slot_capacity, packed,
+                                        reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int32_t sparsp_block_sparse_attn(const sparsp_geometry* geom, const uint16_t* Q, const uint8_t* mask,
+                                 int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed,
+                                 int32_t slot_capacity, float softmax_scale, float* O, float* lse, void* stream) {
+  static const char* fn = "sparsp_block_sparse_attn";
+  sparsp::Dims d;
+  int32_t st = check_geometry(geom, fn, &d);
+  if (st) return st;
+  if ((st = check_mask(d, mask, mask_pitch, fn))) return st;
+  if (d.Lq > 0 && (!Q || !slot_of || !packed || !O || !lse)) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
+  if (slot_capacity < 0) return fail(SPARSP_ERR_INVALID, fn, "slot_capacity must be >= 0");
+  if (!isfinite(softmax_scale)) return fail(SPARSP_ERR_INVALID, fn, "softmax_scale must be finite");
+  if ((Q && !aligned16(Q)) || (packed && !aligned16(packed)) || (O && !aligned16(O)))
+    return fail(SPARSP_ERR_INVALID, fn, "Q, packed and O must be 16-byte aligned");
+  return hip_status(sparsp::launch_attention(d, Q, mask, mask_pitch, slot_of, packed, slot_capacity, softmax_scale,
+                                             O, lse, reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Pack of the demanded K/V blocks into the compacted buffer (SparSP paper, sections 5.1 and 6.1: only the
+// blocks a consumer selected travel, one contiguous region per source rank; section 6.2: arrived blocks
+// are placed in the attention kernel's layout).  Slot s = (h, j) receives the K block token-major
+// (b x d) followed by the V block transposed (d x b), so the attention kernel's P V product reads
+// key-contiguous V rows.  The copy is HBM-bound: every byte is read once and written once with 16-byte
+// vector accesses; the V transpose happens in registers on 8 x 8 sub-tiles, so no LDS is involved.
+#include "sparsp_internal.h"
+
+namespace sparsp {
+namespace {
+
+constexpr int kPackThreads = 256;
+
+// Transpose an 8 x 8 tile of 16-bit values held as 8 rows of 4 x 32-bit words (two values per word,
+// lower column in the low half).  Output row e holds input column e.
+__device__ __forceinline__ void transpose8x8(const uint32_t (&in)[8][4], uint32_t (&out)[8][4]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a = in[2 * q][e / 2], b = in[2 * q + 1][e / 2];
+      out[e][q] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+  }
+}
+
+template <int D, int B>
+__global__ __launch_bounds__(kPackThreads) void pack_kernel(const uint16_t* __restrict__ K,
+                                                            const uint16_t* __restrict__ V,
+                                                            const int32_t* __restrict__ seg_offsets, int GH,
+                                                            const int32_t* __restrict__ slot_block,
+                                                            const int32_t* __restrict__ slot_head,
+                                                            int slot_capacity, int nb,
+                                                            uint16_t* __restrict__ packed) {
+  constexpr int kSub = (B / 8) * (D / 8);         // 8 x 8 sub-tiles per block
+  constexpr int kSlotsPerWg = kPackThreads / kSub;  // 1, 2 or 4
+  constexpr int kChunksPerThread = 8;               // 16-byte K chunks per thread = (B*D/8) / kSub
+  static_assert(kSub * kSlotsPerWg == kPackThreads, "tile shape");
+  constexpr int64_t kSlotElems = 2ll * B * D;
+
+  const int S = min(seg_offsets[GH], slot_capacity);
+  const int s = blockIdx.x * kSlotsPerWg + threadIdx.x / kSub;
+  if (s >= S) return;
+  const int u = threadIdx.x % kSub;
+  const int h = slot_head[s], j = slot_block[s];
+  const int64_t src = ((int64_t)h * nb + j) * B * D;
+  uint16_t* dst = packed + (int64_t)s * kSlotElems;
+
+  // K: a straight copy; consecutive threads move consecutive 16-byte chunks.
+  uint4 kv[kChunksPerThread];
+#pragma unroll
+  for (int i = 0; i < kChunksPerThread; ++i)
+    kv[i] = *reinterpret_cast<const uint4*>(K + src + (int64_t)(u + i * kSub) * 8);
+
+  // V: sub-tile (g, c) = keys 8g..8g+7, columns 8c..8c+7; consecutive threads take consecutive column
+  // chunks of the same rows, so the loads stay coalesced.
+  const int c = u % (D / 8), g = u / (D / 8);
+  uint32_t vin[8][4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint4 v = *reinterpret_cast<const uint4*>(V + src + (int64_t)(g * 8 + i) * D + c * 8);
+    vin[i][0] = v.x;
+    vin[i][1] = v.y;
+    vin[i][2] = v.z;
+    vin[i][3] = v.w;
+  }
+
+#pragma unroll
+  for (int i = 0; i < kChunksPerThread; ++i) *reinterpret_cast<uint4*>(dst + (int64_t)(u + i * kSub) * 8) = kv[i];
+
+  uint32_t vout[8][4];
+  transpose8x8(vin, vout);
+  uint16_t* vt = dst + (int64_t)B * D;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    *reinterpret_cast<uint4*>(vt + (int64_t)(c * 8 + e) * B + g * 8) =
+        make_uint4(vout[e][0], vout[e][1], vout[e][2], vout[e][3]);
+}
+
+template <int D, int B>
+hipError_t launch_pack_t(const Dims& g, const uint16_t* K, const uint16_t* V, const int32_t* seg_offsets,
+                         const int32_t* slot_block, const int32_t* slot_head, int32_t slot_capacity,
+                         uint16_t* packed, hipStream_t stream) {
+  constexpr int kSlotsPerWg = kPackThreads / ((B / 8) * (D / 8));
+  const int64_t hnb = (int64_t)g.H * g.nb;  // S never exceeds H*nb
+  const int64_t cap = slot_capacity < hnb ? (int64_t)slot_capacity : hnb;
+  const unsigned grid = (unsigned)((cap + kSlotsPerWg - 1) / kSlotsPerWg);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((pack_kernel<D, B>), dim3(grid), dim3(kPackThreads), 0, stream, K, V, seg_offsets, g.G * g.H,
+                     slot_block, slot_head, (int)cap, g.nb, packed);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pack(const Dims& g, const uint16_t* K, const uint16_t* V, const int32_t* seg_offsets,
+                       const int32_t* slot_block, const int32_t* slot_head, int32_t slot_capacity,
+                       uint16_t* packed, hipStream_t stream) {
+  if (g.d == 128 && g.b == 128)
+    return launch_pack_t<128, 128>(g, K, V, seg_offsets, slot_block, slot_head, slot_capacity, packed, stream);
+  if (g.d == 64 && g.b == 64)
+    return launch_pack_t<64, 64>(g, K, V, seg_offsets, slot_block, slot_head, slot_capacity, packed, stream);
+  if (g.d == 128 && g.b == 64)
+    return launch_pack_t<128, 64>(g, K, V, seg_offsets, slot_block, slot_head, slot_capacity, packed, stream);
+  return launch_pack_t<64, 128>(g, K, V, seg_offsets, slot_block, slot_head, slot_capacity, packed, stream);
+}
+
+}  // namespace sparsp

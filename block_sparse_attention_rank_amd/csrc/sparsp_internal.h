@@ -1,0 +1,47 @@
+// Internal declarations shared by the HIP translation units of libsparsp (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sparsp {
+
+// Sizes derived from the public geometry after validation.
+struct Dims {
+  int H, d, b, N, G, r, Lq;
+  int nb;  // ceil(N / b)
+  int W;   // ceil(nb / 64)
+};
+
+constexpr int kMaxRanks = 64;
+constexpr int kMaxBlocks = 16384;
+constexpr int kCompactLdsLimit = 64 * 1024;
+
+inline size_t compact_lds_bytes(const Dims& g) {
+  return (size_t)g.G * g.W * 12 + ((size_t)g.G * g.H + 1) * 4;
+}
+
+hipError_t launch_union(const Dims& g, const uint8_t* mask, int64_t pitch, uint64_t* demand,
+                        hipStream_t stream);
+hipError_t launch_compact(const Dims& g, const int32_t* placement, const uint64_t* demand,
+                          int32_t* seg_offsets, int32_t* slot_block, int32_t* slot_head,
+                          int32_t* slot_of, hipStream_t stream);
+hipError_t launch_pack(const Dims& g, const uint16_t* K, const uint16_t* V, const int32_t* seg_offsets,
+                       const int32_t* slot_block, const int32_t* slot_head, int32_t slot_capacity,
+                       uint16_t* packed, hipStream_t stream);
+hipError_t launch_attention(const Dims& g, const uint16_t* Q, const uint8_t* mask, int64_t pitch,
+                            const int32_t* slot_of, const uint16_t* packed, int32_t slot_capacity,
+                            float softmax_scale, float* O, float* lse, hipStream_t stream);
+
+// Number of XCDs whose L2 slices a launch is spread over (MI355X: 8).  Workgroup ids are handed to the
+// XCDs round-robin, so kernels that want neighbouring work items to share an L2 remap their ids.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int xcd_remap(int pid, int total) {
+  const int xcd = pid % kXcds, idx = pid / kXcds;
+  const int base = total / kXcds, rem = total % kXcds;
+  const int start = xcd < rem ? xcd * (base + 1) : rem * (base + 1) + (xcd - rem) * base;
+  return start + idx;
+}
+
+}  // namespace sparsp

@@ -1,0 +1,157 @@
+/*
+ * sparsp.h -- C ABI for one sequence-parallel rank's share of block-sparse attention on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operations follow "SparSP: Exploiting Communication Sparsity for Sequence-Parallel Video DiTs"
+ * (full text, paperpeel.com page): a token sequence is cut into blocks of b tokens, every head h has a
+ * block mask M[h, i, j] (query block i may attend to key block j), and a placement P assigns every block
+ * to one of G sequence-parallel ranks.  For the queries of rank r the library computes
+ *
+ *   1. sparsp_local_query_blocks  -- Q_r = {i : P(i) = r}, ascending (section 4.1, Eq. 2).
+ *   2. sparsp_demand_union        -- the per-head demand union of Eq. 2 (section 4.1) kept per head
+ *                                    (section 5.2, head-preserving demand), and its compaction into
+ *                                    packed slots enumerated by (source rank, head, block) in row-major
+ *                                    order (section 5.2, metadata-free exchange).
+ *   3. sparsp_pack_kv             -- the demanded K/V blocks copied into one compacted buffer whose
+ *                                    per-source-rank segments are the payloads that would cross the
+ *                                    link (sections 5.1 and 6.1), already in the attention kernel's
+ *                                    layout (section 6.2 places arrived blocks into that layout).
+ *   4. sparsp_block_sparse_attn   -- softmax(Q K^T / sqrt(d)) V (section 2.2) over the selected key
+ *                                    blocks only, with an online softmax (section 2.3), reading K/V
+ *                                    from the compacted buffer.
+ *
+ * Conventions shared by every call
+ *   - bf16 tensors are passed as uint16_t bit patterns (IEEE bfloat16).
+ *   - Device pointers point to memory on the current HIP device and are owned by the caller.  The
+ *     library allocates nothing, keeps no state between calls and never synchronises: work is enqueued
+ *     on `stream` (a hipStream_t; NULL = the legacy default stream) in call order.
+ *   - Arguments are checked before anything is launched; a failed check returns an error status and
+ *     launches nothing.  Contents of device arrays (mask bytes, placement values) are not checked on
+ *     the host; the kernels never read or write outside the documented extents even when they are
+ *     inconsistent (out-of-range values are treated as "not selected").
+ *   - SPARSP_ERR_HIP reports a launch failure; asynchronous device faults surface at the caller's next
+ *     synchronisation.  sparsp_last_error() returns a message for the calling thread's last failure.
+ *   - Every call is re-entrant and thread-safe.
+ *
+ * Geometry: nb = ceil(N / b) blocks; W = ceil(nb / 64) demand words per head.  Supported: d in {64, 128},
+ * b in {64, 128}, 1 <= G <= 64, nb <= 16384, 0 <= Lq <= nb, H >= 1, 0 <= r < G.
+ */
+#ifndef SPARSP_H
+#define SPARSP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPARSP_ABI_VERSION 1
+
+typedef enum sparsp_status {
+  SPARSP_OK = 0,
+  SPARSP_ERR_INVALID = 1,      /* null pointer, bad size, stride or alignment                       */
+  SPARSP_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels implement (d, b, G, nb limits)  */
+  SPARSP_ERR_HIP = 3           /* the HIP runtime reported an error while launching                 */
+} sparsp_status;
+
+typedef struct sparsp_geometry {
+  int32_t H;   /* heads                                                    */
+  int32_t d;   /* head dimension (64 or 128)                               */
+  int32_t b;   /* tokens per block (64 or 128)                             */
+  int32_t N;   /* real tokens in the whole sequence (nb = ceil(N / b))      */
+  int32_t G;   /* sequence-parallel ranks                                  */
+  int32_t r;   /* the rank whose share is computed                         */
+  int32_t Lq;  /* number of local query blocks, |Q_r|                      */
+} sparsp_geometry;
+
+/* ABI version (SPARSP_ABI_VERSION of the built library). */
+int32_t sparsp_abi_version(void);
+
+/* Static description of a status code. */
+const char* sparsp_status_string(int32_t status);
+
+/* Message describing the calling thread's most recent failed call ("" if none). */
+const char* sparsp_last_error(void);
+
+/*
+ * Q_r = {i : P(i) = r} in ascending order (section 4.1, Eq. 2; section 4.3 computes the placement once
+ * per geometry, off the critical path).  HOST pointers.
+ *   placement  [nb] int32, values in [0, G)           (read)
+ *   q_blocks   [capacity] int32                        (written: the first *Lq entries)
+ *   Lq         int32                                   (written: |Q_r|)
+ * Errors: SPARSP_ERR_INVALID for null pointers, nb < 1, r outside [0, G), a placement value outside
+ * [0, G), or capacity < |Q_r| (then nothing is written to q_blocks and *Lq holds the needed size).
+ */
+int32_t sparsp_local_query_blocks(const int32_t* placement, int32_t nb, int32_t G, int32_t r,
+                                  int32_t* q_blocks, int32_t capacity, int32_t* Lq);
+
+/*
+ * Demand union and per-peer compaction (section 4.1 Eq. 2; section 5.2).  DEVICE pointers.
+ *   mask         [H][Lq][mask_pitch] uint8, the rank's own rows M[h, i in Q_r (ascending), j];
+ *                nonzero = selected; columns j >= nb are ignored.  mask_pitch >= nb, a multiple of 16,
+ *                and mask 16-byte aligned.                                            (read)
+ *   placement    [nb] int32, P(j) in [0, G)                                           (read)
+ *   demand       [H][W] uint64: bit (j mod 64) of word (j / 64) = OR over local rows of M[h, ., j];
+ *                bits >= nb are 0                                                      (written)
+ *   seg_offsets  [G*H + 1] int32: first slot of (source rank p, head h) at index p*H + h,
+ *                exclusive prefix sums of the counts; seg_offsets[G*H] = S, the total slot count
+ *                                                                                      (written)
+ *   slot_block   [H*nb] int32: logical block j of slot s, for s < S                   (written, s < S)
+ *   slot_head    [H*nb] int32: head h of slot s, for s < S                            (written, s < S)
+ *   slot_of      [H][nb] int32: slot of (h, j), or -1 if (h, j) is not demanded       (written)
+ * Slots are numbered by source rank p = 0..G-1, then head h = 0..H-1, then ascending j with
+ * P(j) = p, so the blocks owned by rank p form one contiguous range [seg_offsets[p*H], seg_offsets[(p+1)*H])
+ * and each head inside it is contiguous.  The rank's own blocks (p = r) are included.  Results are
+ * deterministic and bit-identical run to run.  slot_block and slot_head must hold H*nb entries (the
+ * worst case), so S never has to be read on the host.
+ * Errors: SPARSP_ERR_INVALID (null pointers, bad sizes, pitch or alignment);
+ * SPARSP_ERR_UNSUPPORTED (G > 64, nb > 16384, or G*W*12 + (G*H+1)*4 bytes above 64 KiB).
+ */
+int32_t sparsp_demand_union(const sparsp_geometry* g, const uint8_t* mask, int64_t mask_pitch,
+                            const int32_t* placement, uint64_t* demand, int32_t* seg_offsets,
+                            int32_t* slot_block, int32_t* slot_head, int32_t* slot_of, void* stream);
+
+/*
+ * Pack the demanded K/V blocks into the compacted buffer (sections 5.1, 6.1, 6.2).  DEVICE pointers.
+ *   K, V         [H][nb*b][d] bf16, token-major; rows >= N should be zero            (read)
+ *   seg_offsets, slot_block, slot_head: as written by sparsp_demand_union            (read)
+ *   slot_capacity  number of slots `packed` can hold (>= 1); slots s >= slot_capacity are not written
+ *   packed       [slot_capacity][2][b*d] bf16.  Slot s = (h, j) = (slot_head[s], slot_block[s]) holds
+ *                  part 0: K[h, j*b + t, c] at t*d + c        (the K block, token-major, b x d)
+ *                  part 1: V[h, j*b + t, c] at c*b + t        (the V block transposed, d x b)
+ *                for every s < min(S, slot_capacity); other slots are left untouched  (written)
+ * Errors: SPARSP_ERR_INVALID (null pointers, slot_capacity < 1, misaligned K/V/packed: 16 bytes);
+ * SPARSP_ERR_UNSUPPORTED (d or b outside {64, 128}).
+ */
+int32_t sparsp_pack_kv(const sparsp_geometry* g, const uint16_t* K, const uint16_t* V,
+                       const int32_t* seg_offsets, const int32_t* slot_block, const int32_t* slot_head,
+                       int32_t slot_capacity, uint16_t* packed, void* stream);
+
+/*
+ * Block-sparse flash attention for the local queries over the compacted K/V (sections 2.2, 2.3; Eq. 2's
+ * mask).  DEVICE pointers.
+ *   Q            [H][Lq*b][d] bf16: local query rows, blocks in Q_r order             (read)
+ *   mask         as for sparsp_demand_union                                           (read)
+ *   slot_of      [H][nb] int32 from sparsp_demand_union on the same mask              (read)
+ *   packed       [slot_capacity][2][b*d] from sparsp_pack_kv                          (read)
+ *   softmax_scale  multiplies Q K^T before the softmax (1/sqrt(d) for the paper's formula)
+ *   O            [H][Lq*b][d] float32: softmax-weighted sum of V rows                  (written)
+ *   lse          [H][Lq*b] float32: natural-log log-sum-exp of the scaled logits       (written)
+ * For local block k of head h the keys are the real tokens (index < N) of every block j with
+ * mask[h][k][j] != 0, visited in ascending j; key tokens of the last block at index >= N are excluded.
+ * A row with no key gives O = 0 and lse = -inf.  A selected block whose slot_of entry is negative or
+ * >= slot_capacity is skipped.  Inputs are bf16; products accumulate in fp32 and the softmax
+ * probabilities are rounded to bf16 before the P V product.
+ * Errors: SPARSP_ERR_INVALID (null pointers, bad sizes, pitch, alignment, non-finite scale);
+ * SPARSP_ERR_UNSUPPORTED (d or b outside {64, 128}, nb > 16384).
+ */
+int32_t sparsp_block_sparse_attn(const sparsp_geometry* g, const uint16_t* Q, const uint8_t* mask,
+                                 int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed,
+                                 int32_t slot_capacity, float softmax_scale, float* O, float* lse,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSP_H */

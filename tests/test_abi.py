@@ -1,0 +1,121 @@
+"""The C ABI without a GPU: the library loads, exports every symbol include/sparsp.h declares, and the
+host-side logic (status strings, the local-set call, argument checks) behaves as documented.  No call
+here reaches a kernel launch: every device entry point is called with arguments it must reject first."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import block_sparse_attention_rank_amd as bsa
+import oracle as O
+from block_sparse_attention_rank_amd import _lib
+from workloads import placement_contiguous, placement_periodic
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparsp.h")
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparsp_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = bsa.load()
+    declared = _declared_symbols()
+    assert set(declared) == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    lib = bsa.load()
+    assert lib.sparsp_abi_version() == 1
+    assert lib.sparsp_status_string(0) == b"ok"
+    assert lib.sparsp_status_string(1) == b"invalid argument"
+    assert lib.sparsp_status_string(2) == b"unsupported configuration"
+    assert lib.sparsp_status_string(3) == b"HIP runtime error"
+    assert lib.sparsp_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("placement", [placement_contiguous(929, 8), placement_periodic(929, 128, 3600, 8),
+                                       placement_periodic(3072, 64, 6144, 8)])
+def test_local_query_blocks_matches_oracle(placement):
+    G = int(placement.max()) + 1
+    for r in range(G):
+        assert np.array_equal(bsa.local_query_blocks(placement, G, r), O.local_query_blocks(placement, r))
+
+
+def test_local_query_blocks_errors():
+    lib = bsa.load()
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    P = np.array([0, 1, 2, 5], np.int32)                 # 5 is outside [0, G) for G = 4
+    out = np.zeros(4, np.int32)
+    n = ctypes.c_int32(-1)
+    st = lib.sparsp_local_query_blocks(P.ctypes.data_as(i32p), 4, 4, 0, out.ctypes.data_as(i32p), 4, ctypes.byref(n))
+    assert st == _lib.SPARSP_ERR_INVALID and b"placement" in lib.sparsp_last_error()
+    P = np.array([0, 0, 0, 1], np.int32)
+    st = lib.sparsp_local_query_blocks(P.ctypes.data_as(i32p), 4, 2, 0, out.ctypes.data_as(i32p), 2, ctypes.byref(n))
+    assert st == _lib.SPARSP_ERR_INVALID and n.value == 3         # needed size reported
+    st = lib.sparsp_local_query_blocks(P.ctypes.data_as(i32p), 4, 2, 2, out.ctypes.data_as(i32p), 4, ctypes.byref(n))
+    assert st == _lib.SPARSP_ERR_INVALID
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails its argument check first
+
+
+def _geom(**kw):
+    base = dict(H=2, d=128, b=128, N=1000, G=4, r=0, Lq=2)
+    base.update(kw)
+    return _lib.Geometry(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(H=0), _lib.SPARSP_ERR_INVALID),
+    (dict(N=0), _lib.SPARSP_ERR_INVALID),
+    (dict(r=4), _lib.SPARSP_ERR_INVALID),
+    (dict(r=-1), _lib.SPARSP_ERR_INVALID),
+    (dict(Lq=9), _lib.SPARSP_ERR_INVALID),          # nb = 8
+    (dict(d=96), _lib.SPARSP_ERR_UNSUPPORTED),
+    (dict(b=32), _lib.SPARSP_ERR_UNSUPPORTED),
+    (dict(G=65, r=0), _lib.SPARSP_ERR_UNSUPPORTED),
+    (dict(N=128 * 16385, Lq=1), _lib.SPARSP_ERR_UNSUPPORTED),
+])
+def test_geometry_checks(kw, status):
+    lib = bsa.load()
+    g = _geom(**kw)
+    assert lib.sparsp_demand_union(ctypes.byref(g), FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
+    assert lib.sparsp_pack_kv(ctypes.byref(g), FAKE, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None) == status
+    assert lib.sparsp_block_sparse_attn(ctypes.byref(g), FAKE, FAKE, 64, FAKE, FAKE, 4, 0.1, FAKE, FAKE, None) == status
+    assert lib.sparsp_last_error() != b""
+
+
+def test_argument_checks():
+    lib = bsa.load()
+    g = _geom()
+    gp = ctypes.byref(g)
+    E = _lib.SPARSP_ERR_INVALID
+    assert lib.sparsp_demand_union(None, FAKE, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E
+    assert lib.sparsp_demand_union(gp, FAKE, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E      # pitch < nb
+    assert lib.sparsp_demand_union(gp, FAKE, 24, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E     # not 16-aligned
+    assert lib.sparsp_demand_union(gp, FAKE + 8, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E  # misaligned
+    assert lib.sparsp_demand_union(gp, FAKE, 64, None, FAKE, FAKE, FAKE, FAKE, FAKE, None) == E
+    assert lib.sparsp_pack_kv(gp, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, None) == E                  # capacity
+    assert lib.sparsp_pack_kv(gp, FAKE + 2, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None) == E              # alignment
+    assert lib.sparsp_pack_kv(gp, FAKE, None, FAKE, FAKE, FAKE, 4, FAKE, None) == E
+    assert lib.sparsp_block_sparse_attn(gp, FAKE, FAKE, 64, FAKE, FAKE, 4, float("nan"), FAKE, FAKE, None) == E
+    assert lib.sparsp_block_sparse_attn(gp, None, FAKE, 64, FAKE, FAKE, 4, 0.1, FAKE, FAKE, None) == E
+    assert lib.sparsp_block_sparse_attn(gp, FAKE, FAKE, 64, FAKE, FAKE, -1, 0.1, FAKE, FAKE, None) == E
+    assert b"slot_capacity" in lib.sparsp_last_error()
+
+
+def test_compaction_lds_limit():
+    """A geometry whose compaction tables exceed 64 KiB of LDS is refused, not launched."""
+    lib = bsa.load()
+    g = _geom(H=64, G=64, r=0, b=64, N=64 * 16384, Lq=1)       # W = 256: 64*256*12 bytes > 64 KiB
+    pitch = 16384
+    assert lib.sparsp_demand_union(ctypes.byref(g), FAKE, pitch, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None) == _lib.SPARSP_ERR_UNSUPPORTED

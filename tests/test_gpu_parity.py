@@ -1,0 +1,190 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle on the same seeded inputs.
+
+Union, compaction indices and packed bytes must be bit-exact.  Attention outputs (bf16 inputs, fp32
+accumulation, bf16 probabilities in the P V product) must lie within max |dO| <= 1e-2 and
+mean |dO| <= 1e-3 of the oracle over real query rows; lse within 1e-3 * max(1, |lse|).
+Full-size workloads are checked on sampled (head, query block) pairs that the oracle computes one by
+one, chosen to include the last block (key padding), the heaviest and lightest heads, and the first and
+last heads.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from workloads import CONFIGS, custom, make_inputs
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS = 1e-2, 1e-3
+_cache = {}
+
+
+def _inputs(name):
+    if name not in _cache:
+        _cache.clear()                     # keep one full-size workload in memory at a time
+        _cache[name] = make_inputs(name)
+    return _cache[name]
+
+
+def _oracle_union(inp):
+    w = inp["workload"]
+    U = O.demand_union(inp["mask"], w.nb)
+    return U, O.compact(U, inp["placement"], w.G)
+
+
+def _check_union(got, inp):
+    U, c = _oracle_union(inp)
+    assert np.array_equal(got["demand"], O.demand_words(U))
+    assert np.array_equal(got["seg_offsets"], c["seg_offsets"])
+    assert got["S"] == c["S"]
+    assert np.array_equal(got["slot_block"], c["slot_block"])
+    assert np.array_equal(got["slot_head"], c["slot_head"])
+    assert np.array_equal(got["slot_of"], c["slot_of"])
+    return c
+
+
+def _check_attention(inp, O_dev, lse_dev, items):
+    w = inp["workload"]
+    b = w.b
+    scale = 1.0 / math.sqrt(w.d)
+    errs, lse_errs = [], []
+    for h, k in items:
+        Oo, lo = O.attention_block(inp["Q"], inp["K"], inp["V"], inp["mask"], h, k, b, w.N, scale)
+        rows = O.real_rows(inp["q_blocks"][k:k + 1], b, w.N)
+        got = O_dev[h, k * b:(k + 1) * b][rows]
+        errs.append(np.abs(got - Oo[rows]))
+        gl, ol = lse_dev[h, k * b:(k + 1) * b][rows], lo[rows]
+        finite = np.isfinite(ol)
+        assert np.array_equal(np.isfinite(gl), finite)
+        if finite.any():
+            lse_errs.append(np.abs(gl[finite] - ol[finite]) / np.maximum(1.0, np.abs(ol[finite])))
+        if not finite.all():
+            assert np.all(got[~finite] == 0)
+    e = np.concatenate([x.ravel() for x in errs])
+    assert e.max() <= MAX_ABS, f"max |dO| = {e.max():.3e}"
+    assert e.mean() <= MEAN_ABS, f"mean |dO| = {e.mean():.3e}"
+    if lse_errs:
+        le = np.concatenate(lse_errs)
+        assert le.max() <= 1e-3, f"max rel |dlse| = {le.max():.3e}"
+    return e.max(), e.mean()
+
+
+def _sample_items(inp, n_rand=6, seed=0):
+    w = inp["workload"]
+    H, Lq = w.H, len(inp["q_blocks"])
+    per_head = inp["mask"][:, :, :w.nb].sum((1, 2))
+    heavy, light = int(np.argmax(per_head)), int(np.argmin(per_head))
+    rng = np.random.default_rng(seed)
+    items = {(0, 0), (H - 1, Lq - 1), (heavy, Lq // 2), (light, 0), (heavy, Lq - 1)}
+    last = np.flatnonzero(inp["mask"][:, :, w.nb - 1].any(0))   # rows that select the padded last block
+    if len(last):
+        items.add((int(np.argmax(inp["mask"][:, last[0], w.nb - 1])), int(last[0])))
+    for _ in range(n_rand):
+        items.add((int(rng.integers(H)), int(rng.integers(Lq))))
+    return sorted(items)
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_union_compaction_pack_bit_exact(require_gpu, name):
+    from _gpu import run_path, to_host_u16, union_host
+    inp = _inputs(name)
+    w = inp["workload"]
+    print(f"[parity] union/pack {name}", flush=True)
+    res = run_path(inp, attention=False)
+    c = _check_union(union_host(res["union"]), inp)
+    packed = to_host_u16(res["packed"][:c["S"]])
+    expect = O.pack(inp["K"], inp["V"], c["slot_block"], c["slot_head"], w.b)
+    assert np.array_equal(packed, expect)
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+def test_attention_matches_oracle(require_gpu, name):
+    from _gpu import run_path
+    inp = _inputs(name)
+    w = inp["workload"]
+    print(f"[parity] attention {name}", flush=True)
+    res = run_path(inp)
+    Od, ld = res["O"].cpu().numpy(), res["lse"].cpu().numpy()
+    Lq = len(inp["q_blocks"])
+    if w.H * Lq <= 300:
+        items = [(h, k) for h in range(w.H) for k in range(Lq)]
+    else:
+        items = _sample_items(inp)
+    mx, mean = _check_attention(inp, Od, ld, items)
+    print(f"[parity] {name}: {len(items)} blocks, max {mx:.2e}, mean {mean:.2e}", flush=True)
+
+
+EDGE_CASES = {
+    "pad_d128_b128": custom(H=3, d=128, b=128, T=3, HW=300, G=2, r=1, density=0.5),
+    "pad_d64_b64": custom(H=2, d=64, b=64, T=5, HW=100, G=3, r=2, density=0.4),
+    "d128_b64": custom(H=2, d=128, b=64, T=4, HW=256, G=4, r=3, placement="periodic", density=0.3),
+    "d64_b128": custom(H=2, d=64, b=128, T=4, HW=384, G=2, r=0, density=0.5),
+    "all_ones": custom(H=2, d=128, b=128, T=2, HW=700, G=2, r=0, mask_kind="ones"),
+    "identity": custom(H=2, d=64, b=64, T=3, HW=256, G=3, r=1, mask_kind="identity"),
+    "empty_rows": custom(H=2, d=64, b=64, T=2, HW=256, G=2, r=0, mask_kind="zeros"),
+    "single_rank": custom(H=1, d=128, b=128, T=2, HW=640, G=1, r=0, density=0.3),
+    "k_offsets": custom(H=2, d=64, b=64, T=4, HW=512, G=2, r=1, k_offset_sigma=6.0, density=0.2),
+    "many_ranks": custom(H=2, d=64, b=64, T=8, HW=1024, G=64, r=62, placement="periodic", density=0.1),
+    "wide_row": custom(H=1, d=128, b=128, T=2, HW=128 * 150, G=2, r=1, density=0.45),
+}
+
+
+@pytest.mark.parametrize("case", list(EDGE_CASES))
+def test_edge_cases(require_gpu, case):
+    from _gpu import run_path, to_host_u16, union_host
+    w = EDGE_CASES[case]
+    inp = make_inputs(w)
+    print(f"[parity] edge {case}: H={w.H} d={w.d} b={w.b} N={w.N} G={w.G} r={w.r}", flush=True)
+    res = run_path(inp)
+    c = _check_union(union_host(res["union"]), inp)
+    assert np.array_equal(to_host_u16(res["packed"][:c["S"]]),
+                          O.pack(inp["K"], inp["V"], c["slot_block"], c["slot_head"], w.b))
+    Lq = len(inp["q_blocks"])
+    items = [(h, k) for h in range(w.H) for k in range(Lq)]
+    _check_attention(inp, res["O"].cpu().numpy(), res["lse"].cpu().numpy(), items)
+
+
+def test_no_local_blocks(require_gpu):
+    """A rank that owns no block (Lq = 0): the demand is empty and attention launches nothing."""
+    from _gpu import run_path, union_host
+    w = custom(H=2, d=64, b=64, T=1, HW=128, G=4, r=3)          # nb = 2 < G: rank 3 owns nothing
+    inp = make_inputs(w)
+    assert len(inp["q_blocks"]) == 0
+    res = run_path(inp)
+    got = union_host(res["union"])
+    assert got["S"] == 0 and np.all(got["slot_of"] == -1) and not got["demand"].any()
+    assert res["O"].numel() == 0
+
+
+def test_pack_respects_capacity(require_gpu):
+    """slot_capacity below S truncates the pack; nothing past the capacity is written."""
+    import torch
+    import block_sparse_attention_rank_amd as bsa
+    from _gpu import run_path, to_host_u16, union_host
+    w = custom(H=2, d=64, b=64, T=2, HW=512, G=2, r=0, density=0.6)
+    inp = make_inputs(w)
+    res = run_path(inp, attention=False)
+    got = union_host(res["union"])
+    cap = got["S"] // 2
+    buf = torch.full((got["S"], 2, w.b * w.d), 7.0, dtype=torch.bfloat16, device="cuda")
+    bsa.pack_kv(res["g"], res["dev"]["K"], res["dev"]["V"], res["union"], out=buf[:cap])
+    torch.cuda.synchronize()
+    expect = O.pack(inp["K"], inp["V"], got["slot_block"], got["slot_head"], w.b)
+    host = to_host_u16(buf)
+    assert np.array_equal(host[:cap], expect[:cap])
+    assert np.all(host[cap:] == 0x40E0)                          # bf16 7.0 untouched
+
+
+def test_repeat_runs_are_bit_identical(require_gpu):
+    from _gpu import run_path, to_host_u16
+    inp = make_inputs(custom(H=3, d=128, b=128, T=3, HW=1000, G=4, r=1, density=0.4))
+    a = run_path(inp)
+    b = run_path(inp, dev=a["dev"])
+    for key in ("seg_offsets", "slot_of", "demand"):
+        assert np.array_equal(getattr(a["union"], key).cpu().numpy(), getattr(b["union"], key).cpu().numpy())
+    S = int(a["union"].seg_offsets[-1].item())
+    assert np.array_equal(to_host_u16(a["packed"][:S]), to_host_u16(b["packed"][:S]))
+    assert np.array_equal(a["O"].cpu().numpy(), b["O"].cpu().numpy())
+    assert np.array_equal(a["lse"].cpu().numpy(), b["lse"].cpu().numpy())
