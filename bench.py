@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--config", default="hunyuan")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle attention sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="after the warmup, run one plain float32 device copy of this many MiB (read + write of "
+                         "known size) so profiler byte counters can be scaled against it")
     return ap.parse_args()
 
 
@@ -167,6 +170,13 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     S = int(u.seg_offsets[-1].item())
     seg = u.seg_offsets.cpu().numpy()
     own_lo, own_hi = int(seg[w.r * g.H]), int(seg[(w.r + 1) * g.H])
