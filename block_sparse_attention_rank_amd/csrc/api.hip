@@ -144,7 +144,8 @@ int32_t sparsp_block_sparse_attn(const sparsp_geometry* geom, const uint16_t* Q,
   if ((st = check_mask(d, mask, mask_pitch, fn))) return st;
   if (d.Lq > 0 && (!Q || !slot_of || !packed || !O || !lse)) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
   if (slot_capacity < 0) return fail(SPARSP_ERR_INVALID, fn, "slot_capacity must be >= 0");
-  if (!isfinite(softmax_scale)) return fail(SPARSP_ERR_INVALID, fn, "softmax_scale must be finite");
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(SPARSP_ERR_INVALID, fn, "softmax_scale must be finite and positive");
   if ((Q && !aligned16(Q)) || (packed && !aligned16(packed)) || (O && !aligned16(O)))
     return fail(SPARSP_ERR_INVALID, fn, "Q, packed and O must be 16-byte aligned");
   return hip_status(sparsp::launch_attention(d, Q, mask, mask_pitch, slot_of, packed, slot_capacity, softmax_scale,

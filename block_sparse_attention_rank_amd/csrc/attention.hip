@@ -32,13 +32,14 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;  // 16 bytes; a native vector so it stays in VGPRs
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 constexpr int kStageKeys = 64;     // keys per pipeline stage
-constexpr int kListCap = 1024;     // selected blocks listed per pass over the mask row
+constexpr int kListCap = 512;      // selected blocks listed per pass over the mask row
 constexpr float kRescaleLog2 = 8.f;
 
 template <int D, int B>
@@ -46,51 +47,48 @@ struct Tile {
   static constexpr int NW = B / 32;                      // waves, 32 query rows each
   static constexpr int NT = NW * 64;                     // threads
   static constexpr int NST = B / kStageKeys;             // stages per key block
-  static constexpr int KP = D * 2 + 16;                  // LDS bytes per K row (16-byte pad)
-  static constexpr int VP = kStageKeys * 2 + 16;         // LDS bytes per V^T row (16-byte pad)
-  static constexpr int KBYTES = kStageKeys * KP;         // K part of a stage in LDS
-  static constexpr int VBYTES = D * VP;                  // V^T part of a stage in LDS
-  static constexpr int KCH = kStageKeys * D / 8;         // 16-byte chunks of K per stage
-  static constexpr int CH = 2 * KCH;                     // ... of K and V^T
-  static constexpr int CPT = CH / NT;                    // chunks per thread per stage
+  // LDS row pitches.  The LDS serves 128 bytes per clock from 32 four-byte banks: 8 lanes of a 16-byte
+  // access or 16 lanes of an 8-byte access.  The fragment reads take one column of consecutive rows, so a
+  // K row pitch of 4 (mod 32) words and a V^T row pitch of 2 (mod 32) words put those lanes on distinct
+  // banks; the stores write 128 contiguous bytes per clock.
+  static constexpr int KP = D * 2 + 16;                  // bytes per K row, 16-byte aligned
+  static constexpr int VP = kStageKeys * 2 + 8;          // bytes per V^T row, 8-byte aligned
+  static constexpr int KBYTES = kStageKeys * KP;         // K part of a stage buffer
+  static constexpr int STAGE = KBYTES + D * VP;          // one stage buffer
+  static constexpr int KCH = kStageKeys * D / 8;         // 16-byte chunks of K per stage (same for V^T)
+  static constexpr int KCPT = KCH / NT;                  // K chunks per thread per stage (same for V^T)
   static constexpr int NDT = D / 32;                     // 32-row tiles of O^T
   static constexpr int NQF = D / 16;                     // Q fragments along d
   static constexpr int64_t SLOT = 2ll * B * D;           // elements per packed slot
-  static_assert(CH % NT == 0, "stage must split evenly over the threads");
+  static_assert(KCH % NT == 0, "stage must split evenly over the threads");
 };
 
-// Global element offset (within a slot) and LDS byte offset of the q-th 16-byte chunk of stage hh.
-// Rows are padded by 16 bytes: consecutive rows start 4 banks apart, so the 8 (16-byte reads) or 16
-// (8-byte reads) lanes the LDS serves per cycle, which read one column of consecutive rows, never collide,
-// and every fragment address is a per-lane base plus a compile-time offset.
-template <int D, int B>
-__device__ __forceinline__ void stage_chunk(int q, int hh, int64_t& gofs, int& lofs) {
+// Issue this thread's global loads of stage hh of a packed slot (K rows hh*64.., V^T columns hh*64..).
+template <int D, int B, int N2>
+__device__ __forceinline__ void load_stage(u32x4 (&pre)[N2], const char* __restrict__ slot, int hh, int t) {
   using T = Tile<D, B>;
-  if (q < T::KCH) {
-    const int r = q / (D / 8), c = q % (D / 8);
-    gofs = (int64_t)(hh * kStageKeys + r) * D + c * 8;
-    lofs = r * T::KP + c * 16;
-  } else {
-    const int qq = q - T::KCH;
-    const int dd = qq / 8, c = qq % 8;
-    gofs = (int64_t)B * D + (int64_t)dd * B + hh * kStageKeys + c * 8;
-    lofs = T::KBYTES + dd * T::VP + c * 16;
+  static_assert(N2 == 2 * T::KCPT, "one register per chunk");
+  const char* k = slot + hh * (kStageKeys * D * 2);
+  const char* v = slot + (int64_t)B * D * 2 + hh * (kStageKeys * 2);
+#pragma unroll
+  for (int i = 0; i < T::KCPT; ++i) {
+    const int q = t + i * T::NT;
+    pre[i] = *reinterpret_cast<const u32x4*>(k + (unsigned)((q / (D / 8)) * D + (q % (D / 8)) * 8) * 2u);
+    pre[T::KCPT + i] = *reinterpret_cast<const u32x4*>(v + (unsigned)((q / 8) * B + (q % 8) * 8) * 2u);
   }
 }
 
-// Issue the global loads of stage hh of packed slot `slot` into this thread's registers.
-template <int D, int B, int NPRE>
-__device__ __forceinline__ void load_stage(u32x4 (&pre)[NPRE], const uint16_t* __restrict__ packed, int slot,
-                                           int hh, int t) {
+// Write the registers of the loaded stage into an LDS stage buffer.
+template <int D, int B, int N2>
+__device__ __forceinline__ void store_stage(const u32x4 (&pre)[N2], unsigned char* buf, int t) {
   using T = Tile<D, B>;
-  static_assert(NPRE == T::CPT, "one register per chunk");
-  const uint16_t* src = packed + (int64_t)slot * T::SLOT;
 #pragma unroll
-  for (int i = 0; i < T::CPT; ++i) {
-    int64_t g;
-    int l;
-    stage_chunk<D, B>(t + i * T::NT, hh, g, l);
-    pre[i] = *reinterpret_cast<const u32x4*>(src + g);
+  for (int i = 0; i < T::KCPT; ++i) {
+    const int q = t + i * T::NT;
+    *reinterpret_cast<u32x4*>(buf + (q / (D / 8)) * T::KP + (q % (D / 8)) * 16) = pre[i];
+    unsigned char* vrow = buf + T::KBYTES + (q / 8) * T::VP + (q % 8) * 16;
+    *reinterpret_cast<u32x2*>(vrow) = pre[T::KCPT + i].xy;
+    *reinterpret_cast<u32x2*>(vrow + 8) = pre[T::KCPT + i].zw;
   }
 }
 
@@ -100,7 +98,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const int32_t* __restrict__ slot_of, const uint16_t* __restrict__ packed, int slot_capacity, float scale_log2,
     int Lq, int nb, int N, float* __restrict__ O, float* __restrict__ lse) {
   using T = Tile<D, B>;
-  __shared__ __align__(16) unsigned char sStage[T::KBYTES + T::VBYTES];
+  __shared__ __align__(16) unsigned char sStage[2][T::STAGE];
   __shared__ int sList[kListCap];
   __shared__ int sWaveCnt[T::NW];
 
@@ -126,10 +124,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const uint8_t* mrow = mask + ((int64_t)h * Lq + k) * pitch;
   const int32_t* sof = slot_of + (int64_t)h * nb;
   const int tail_valid = N - (nb - 1) * B;  // real keys in the last block, 1..B
-
-  // LDS bases of this lane's fragment reads: K row qr (+32 per key group), V^T row qr (+32 per d tile).
-  const unsigned char* kbase = sStage + qr * T::KP + half * 16;
-  const unsigned char* vbase = sStage + T::KBYTES + qr * T::VP + half * 8;
+  const char* pk = reinterpret_cast<const char*>(packed);
 
   int col = 0;
   while (col < nb) {
@@ -159,50 +154,53 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     }
 
     const int nstage = total * T::NST;
-    u32x4 pre[T::CPT];
-    if (nstage > 0) load_stage<D, B>(pre, packed, sList[0] >> 1, 0, t);
+    u32x4 pre[2 * T::KCPT];
+    if (nstage > 0) {
+      const int c0 = __builtin_amdgcn_readfirstlane(sList[0]);
+      load_stage<D, B>(pre, pk + (int64_t)(c0 >> 1) * (T::SLOT * 2), 0, t);
+    }
 
     for (int st = 0; st < nstage; ++st) {
-      const int code = sList[st / T::NST];
+      // Double-buffered stages: buffer st&1 was last read by stage st-2, which every wave finished
+      // before the barrier of stage st-1.
+      unsigned char* buf = sStage[st & 1];
+      store_stage<D, B>(pre, buf, t);
+      const int code = __builtin_amdgcn_readfirstlane(sList[st / T::NST]);
       const int hh = st % T::NST;
-      const bool last = (code & 1) != 0;
-      __syncthreads();  // every wave is done reading the previous stage
-#pragma unroll
-      for (int i = 0; i < T::CPT; ++i) {
-        int64_t g;
-        int l;
-        stage_chunk<D, B>(t + i * T::NT, hh, g, l);
-        *reinterpret_cast<u32x4*>(sStage + l) = pre[i];
+      if (st + 1 < nstage) {
+        const int cn = __builtin_amdgcn_readfirstlane(sList[(st + 1) / T::NST]);
+        load_stage<D, B>(pre, pk + (int64_t)(cn >> 1) * (T::SLOT * 2), (st + 1) % T::NST, t);
       }
-      if (st + 1 < nstage) load_stage<D, B>(pre, packed, sList[(st + 1) / T::NST] >> 1, (st + 1) % T::NST, t);
       __syncthreads();
 
-      // S^T = K Q^T for the two 32-key groups of the stage.
+      // S^T = K Q^T for the two 32-key groups of the stage (raw scores).
+      const unsigned char* kb = buf + qr * T::KP + half * 16;
       f32x16 sacc[2];
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
+        sacc[g] = mfma32(*reinterpret_cast<const bf16x8*>(kb + g * 32 * T::KP), qf[0], f32x16{});
 #pragma unroll
-        for (int x = 0; x < 16; ++x) sacc[g][x] = 0.f;
-#pragma unroll
-        for (int f = 0; f < T::NQF; ++f)
-          sacc[g] = mfma32(*reinterpret_cast<const bf16x8*>(kbase + g * 32 * T::KP + f * 32), qf[f], sacc[g]);
+        for (int f = 1; f < T::NQF; ++f)
+          sacc[g] = mfma32(*reinterpret_cast<const bf16x8*>(kb + g * 32 * T::KP + f * 32), qf[f], sacc[g]);
       }
 
-      // sacc[g][4i + r] is key 64*hh + 32g + 8i + 4*half + r of query row qr.
+      // sacc[g][4i + r] is key 64*hh + 32g + 8i + 4*half + r of query row qr.  Key tokens past N (only in
+      // the last block) are masked; the branch is uniform.
+      if ((code & 1) && hh * kStageKeys + kStageKeys > tail_valid) {
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int key = hh * kStageKeys + g * 32 + (x / 4) * 8 + half * 4 + (x % 4);
+            if (key >= tail_valid) sacc[g][x] = -INFINITY;
+          }
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) {
-          float v = sacc[g][x] * scale_log2;
-          if (last) {
-            const int key = hh * kStageKeys + g * 32 + (x / 4) * 8 + half * 4 + (x % 4);
-            if (key >= tail_valid) v = -INFINITY;
-          }
-          sacc[g][x] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[g][x]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;  // scale_log2 > 0: the max commutes with scaling
       if (__ballot(mx > m_run + kRescaleLog2) != 0) {
         const float m_new = fmaxf(m_run, mx);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -217,25 +215,26 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       for (int g = 0; g < 2; ++g)
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-          const float p = __builtin_amdgcn_exp2f(sacc[g][x] - m_run);
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[g][x], scale_log2, -m_run));
           l_run += p;
           pf[g][x / 8][x % 8] = (__bf16)p;
         }
 
       // O^T += V^T P^T.  MFMA (g, hf) covers keys 32g + 16hf + {0..3, 8..11} + 4*half of the stage.
+      const unsigned char* vb = buf + T::KBYTES + qr * T::VP + half * 8;
 #pragma unroll
       for (int i = 0; i < T::NDT; ++i)
 #pragma unroll
         for (int g = 0; g < 2; ++g)
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
-            const unsigned char* vb = vbase + i * 32 * T::VP + (g * 32 + hf * 16) * 2;
-            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vb);
-            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vb + 16);
+            const unsigned char* v = vb + i * 32 * T::VP + (g * 32 + hf * 16) * 2;
+            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(v);
+            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(v + 16);
             oacc[i] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pf[g][hf], oacc[i]);
           }
     }
-    __syncthreads();  // sList is rebuilt by the next pass
+    __syncthreads();  // sList and the stage buffers are reused by the next pass
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);

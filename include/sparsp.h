@@ -134,7 +134,7 @@ int32_t sparsp_pack_kv(const sparsp_geometry* g, const uint16_t* K, const uint16
  *   mask         as for sparsp_demand_union                                           (read)
  *   slot_of      [H][nb] int32 from sparsp_demand_union on the same mask              (read)
  *   packed       [slot_capacity][2][b*d] from sparsp_pack_kv                          (read)
- *   softmax_scale  multiplies Q K^T before the softmax (1/sqrt(d) for the paper's formula)
+ *   softmax_scale  multiplies Q K^T before the softmax (1/sqrt(d) for the paper's formula); finite, > 0
  *   O            [H][Lq*b][d] float32: softmax-weighted sum of V rows                  (written)
  *   lse          [H][Lq*b] float32: natural-log log-sum-exp of the scaled logits       (written)
  * For local block k of head h the keys are the real tokens (index < N) of every block j with
@@ -142,7 +142,7 @@ int32_t sparsp_pack_kv(const sparsp_geometry* g, const uint16_t* K, const uint16
  * A row with no key gives O = 0 and lse = -inf.  A selected block whose slot_of entry is negative or
  * >= slot_capacity is skipped.  Inputs are bf16; products accumulate in fp32 and the softmax
  * probabilities are rounded to bf16 before the P V product.
- * Errors: SPARSP_ERR_INVALID (null pointers, bad sizes, pitch, alignment, non-finite scale);
+ * Errors: SPARSP_ERR_INVALID (null pointers, bad sizes, pitch, alignment, a scale that is not finite and > 0);
  * SPARSP_ERR_UNSUPPORTED (d or b outside {64, 128}, nb > 16384).
  */
 int32_t sparsp_block_sparse_attn(const sparsp_geometry* g, const uint16_t* Q, const uint8_t* mask,

@@ -107,6 +107,8 @@ def test_argument_checks():
     assert lib.sparsp_pack_kv(gp, FAKE + 2, FAKE, FAKE, FAKE, FAKE, 4, FAKE, None) == E              # alignment
     assert lib.sparsp_pack_kv(gp, FAKE, None, FAKE, FAKE, FAKE, 4, FAKE, None) == E
     assert lib.sparsp_block_sparse_attn(gp, FAKE, FAKE, 64, FAKE, FAKE, 4, float("nan"), FAKE, FAKE, None) == E
+    assert lib.sparsp_block_sparse_attn(gp, FAKE, FAKE, 64, FAKE, FAKE, 4, 0.0, FAKE, FAKE, None) == E
+    assert lib.sparsp_block_sparse_attn(gp, FAKE, FAKE, 64, FAKE, FAKE, 4, -0.1, FAKE, FAKE, None) == E
     assert lib.sparsp_block_sparse_attn(gp, None, FAKE, 64, FAKE, FAKE, 4, 0.1, FAKE, FAKE, None) == E
     assert lib.sparsp_block_sparse_attn(gp, FAKE, FAKE, 64, FAKE, FAKE, -1, 0.1, FAKE, FAKE, None) == E
     assert b"slot_capacity" in lib.sparsp_last_error()
