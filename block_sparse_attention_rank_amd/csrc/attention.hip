@@ -18,8 +18,10 @@
 // matching 64 columns of V^T, 2 x 64 x d bf16) is copied from global memory straight into LDS with
 // global_load_lds_dwordx4 (no register staging); the next stage's copy is issued before the current one
 // is computed, into the other of two LDS buffers, and two workgroups share a CU.  LDS rows are
-// XOR-swizzled in 16-byte chunks (chunk c of row m sits at c ^ (m & 7)), which keeps the MFMA fragment
-// reads free of bank conflicts; each lane's fragment addresses are fixed per kernel and the buffer, key
+// XOR-swizzled in 16-byte chunks (chunk c of row m sits at c ^ swizzle(m)).  A 16-byte fragment read
+// is served 16 lanes at a time by 64 four-byte banks (256 bytes per clock), and its lanes read one
+// logical chunk of 16 consecutive rows, so the key gives those rows distinct bank groups; it also keeps
+// any 8 consecutive rows apart.  Each lane's fragment addresses are fixed per kernel; the buffer, key
 // group and d tile are immediate offsets.
 //
 // Softmax.  The running maximum is only raised when some row of the wave grows by more than 2^8 (a
@@ -35,8 +37,9 @@ namespace sparsp {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const void lds_void;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -53,8 +56,26 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima): this lane's LDS-direct copies are done.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// XOR key of the 16-byte chunks of an LDS row of `RowBytes` bytes (256: d = 128 K rows; 128: d = 64 K rows
+// and V^T rows).  A 256-byte row covers all 64 banks, so 16 consecutive rows need 16 distinct keys; two
+// 128-byte rows share the banks, so rows of equal parity among 16 need distinct keys, and so do 8
+// consecutive rows.
+template <int RowBytes>
+__device__ __forceinline__ int swizzle(int row) {
+  static_assert(RowBytes == 128 || RowBytes == 256, "row size");
+  return RowBytes == 256 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
+}
+
+// One LDS-direct copy: every lane moves the 16 bytes at base + voff into LDS at lds + 16 * lane
+// (global_load_lds_dwordx4; `lds` is wave-uniform and goes to M0).  It is issued from inline asm so that
+// the compiler does not track it: its own tracking of such copies is coarse and would wait for every
+// copy in flight before the next LDS read.  The pipeline below orders the copies itself (block_sync),
+// and no copy targets a buffer that is read before the barrier that follows its completion.  The s_nop
+// covers the wait state between the M0 write and the copy.
+__device__ __forceinline__ void copy16(const char* base, uint32_t voff, const unsigned char* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const lds_void*)lds;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
+}
 
 constexpr int kStageKeys = 64;     // keys per pipeline stage
 constexpr int kListCap = 512;      // selected blocks listed per pass over the mask row
@@ -80,7 +101,7 @@ struct Tile {
 };
 
 // Stage-invariant parts of this lane's copies.  Copy i of wave w fills LDS chunks (i*NW + w)*64 + lane,
-// 16 bytes per lane, of the K part and of the V^T part.
+// 16 bytes per lane, of a K buffer and of a V^T buffer.
 template <int D, int B>
 struct CopyPlan {
   using T = Tile<D, B>;
@@ -91,91 +112,127 @@ struct CopyPlan {
 #pragma unroll
     for (int i = 0; i < T::CPT; ++i) {
       const int q = (i * T::NW + wave) * 64 + lane;
-      // K: LDS row m, chunk position cp holds logical chunk cp ^ (m & 7) of key sigma(m).
+      // K: LDS row m, chunk position cp holds logical chunk cp ^ swizzle(m) of key sigma(m).
       const int m = q / (D / 8), cp = q % (D / 8);
-      const int c = cp ^ (m & 7);
+      const int c = cp ^ swizzle<T::KROW>(m);
       const int key = (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
       koff[i] = (uint32_t)(key * (D * 2) + c * 16);
-      // V^T: LDS row e (a d index), chunk position cp holds keys 8 * (cp ^ (e & 7)) .. +7.
+      // V^T: LDS row e (a d index), chunk position cp holds keys 8 * (cp ^ swizzle(e)) .. +7.
       const int e = q / 8, vp = q % 8;
-      const int vc = vp ^ (e & 7);
+      const int vc = vp ^ swizzle<T::VROW>(e);
       voff[i] = (uint32_t)(B * D * 2 + e * (B * 2) + vc * 16);
     }
   }
 
-  // Copy stage hh of the slot at `slot` into the LDS stage buffer `buf`.
-  __device__ __forceinline__ void issue(const char* slot, int hh, unsigned char* buf, int wave) const {
+  // Copy the K rows of stage hh of the slot at `slot` into the LDS buffer `kbuf`.
+  __device__ __forceinline__ void issue_k(const char* slot, int hh, unsigned char* kbuf, int wave) const {
     const char* k = slot + hh * T::KBYTES;
+#pragma unroll
+    for (int i = 0; i < T::CPT; ++i) copy16(k, koff[i], kbuf + (i * T::NW + wave) * 1024);
+  }
+
+  // Copy the V^T columns of stage hh of the slot at `slot` into the LDS buffer `vbuf`.
+  __device__ __forceinline__ void issue_v(const char* slot, int hh, unsigned char* vbuf, int wave) const {
     const char* v = slot + hh * T::VROW;
 #pragma unroll
-    for (int i = 0; i < T::CPT; ++i) {
-      __builtin_amdgcn_global_load_lds(k + koff[i], (lds_void*)(buf + (i * T::NW + wave) * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(v + voff[i], (lds_void*)(buf + T::KBYTES + (i * T::NW + wave) * 1024), 16,
-                                       0, 0);
-    }
+    for (int i = 0; i < T::CPT; ++i) copy16(v, voff[i], vbuf + (i * T::NW + wave) * 1024);
   }
 };
 
-// One stage: scores for 64 keys, online-softmax update, O^T += V^T P^T.
+// Per-lane state of the online softmax and the output accumulator.
 template <int D, int B>
-__device__ __forceinline__ void stage_compute(const unsigned char* buf, const uint32_t (&kread)[Tile<D, B>::NQF],
-                                              const uint32_t (&vread)[4], const bf16x8 (&qf)[Tile<D, B>::NQF],
-                                              f32x16 (&oacc)[Tile<D, B>::NDT], float& m_run, float& l_run,
-                                              float scale_log2, int lim) {
+struct RowState {
   using T = Tile<D, B>;
-  // S^T = K Q^T for the two 32-key groups of the stage (raw scores).
-  f32x16 sacc[2];
-#pragma unroll
-  for (int g = 0; g < 2; ++g) {
-    sacc[g] = f32x16{};
-#pragma unroll
-    for (int f = 0; f < T::NQF; ++f)
-      sacc[g] = mfma32(*reinterpret_cast<const bf16x8*>(buf + kread[f] + g * 32 * T::KROW), qf[f], sacc[g]);
-  }
+  f32x16 oacc[T::NDT];
+  float m_run;  // maximum the probabilities are taken against (log2-scaled logits)
+  float l_run;  // sum of this lane's bf16-rounded probabilities relative to m_run
+};
 
-  // sacc[g][4i + r] is key 32g + 16(i >> 1) + 8 half + 4(i & 1) + r of the stage for query row lane % 32.
-  // Keys at or past `lim` (relative to 8 half) are padding of the last block; the branch is uniform.
-  if (lim < kStageKeys) {
+// A unit is one 32-key group g of a stage.  Its scores S^T = K Q^T come from one MFMA tile:
+// sacc[4i + r] is key 32g + 16(i >> 1) + 8 half + 4(i & 1) + r of the stage for query row lane % 32
+// (the K rows sit in LDS in that permuted order).
+template <int D, int B>
+__device__ __forceinline__ f32x16 unit_scores(const unsigned char* kbuf, int g, const uint32_t (&kread)[Tile<D, B>::NQF],
+                                              const bf16x8 (&qf)[Tile<D, B>::NQF]) {
+  using T = Tile<D, B>;
+  f32x16 sacc = f32x16{};
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+  for (int f = 0; f < T::NQF; ++f)
+    sacc = mfma32(*reinterpret_cast<const bf16x8*>(kbuf + kread[f] + g * 32 * T::KROW), qf[f], sacc);
+  return sacc;
+}
+
+// Prepare the scores of a unit for its probabilities: mask the padding keys of the last block (key
+// offsets at or past `lim` inside the unit, counted from 8 half) and raise the running maximum if some
+// row of the wave needs it.
+template <int D, int B>
+__device__ __forceinline__ void unit_head(f32x16& sacc, RowState<D, B>& rs, float scale_log2, int lim) {
+  using T = Tile<D, B>;
+  if (lim < 32) {
 #pragma unroll
-      for (int x = 0; x < 16; ++x) {
-        const int c = 32 * g + 16 * (x / 8) + 4 * ((x / 4) % 2) + (x % 4);
-        if (c >= lim) sacc[g][x] = -INFINITY;
-      }
+    for (int x = 0; x < 16; ++x) {
+      const int c = 16 * (x / 8) + 4 * ((x / 4) % 2) + (x % 4);
+      if (c >= lim) sacc[x] = -INFINITY;
+    }
   }
   float mx = -INFINITY;
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
-#pragma unroll
-    for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[g][x]);
+  for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[x]);
   mx *= scale_log2;  // scale_log2 > 0: the max commutes with scaling
-  if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleLog2) != 0) {
-    const float m_new = fmaxf(m_run, max_halves(mx));
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
+  if (__builtin_amdgcn_ballot_w64(mx > rs.m_run + kRescaleLog2) != 0) {
+    const float m_new = fmaxf(rs.m_run, max_halves(mx));
+    const float alpha = __builtin_amdgcn_exp2f(rs.m_run - m_new);
+    rs.m_run = m_new;
+    rs.l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < T::NDT; ++i) oacc[i] *= alpha;
+    for (int i = 0; i < T::NDT; ++i) rs.oacc[i] *= alpha;
   }
+}
 
-  bf16x8 pf[4];
+// Probabilities of a unit, rounded to bf16 for the second product; the row sum adds the same rounded
+// values (two per v_dot2 against (1, 1)).  pf[b] holds keys 16b + 8 half + 0..7 of the unit.
+__device__ __forceinline__ void unit_probabilities(const f32x16& sacc, float scale_log2, float m_run, bf16x8 (&pf)[2],
+                                                   float& l_run) {
 #pragma unroll
-  for (int g = 0; g < 2; ++g)
+  for (int x = 0; x < 16; ++x)
+    pf[x / 8][x % 8] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[x], scale_log2, -m_run));
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
+  float l_odd = 0.f;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[g][x], scale_log2, -m_run));
-      l_run += p;
-      pf[2 * g + x / 8][x % 8] = (__bf16)p;
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const bf16x2 pair = {pf[b][e], pf[b][e + 1]};
+      if (e & 2)
+        l_odd = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_odd, false);
+      else
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_run, false);
     }
+  l_run += l_odd;
+}
 
-  // O^T += V^T P^T: step a covers keys 16a + 8 half + 0..7 of the stage, which is one V^T fragment.
+// O^T += V^T P^T for unit g: step b covers keys 32g + 16b + 8 half + 0..7 of the stage, one V^T fragment.
+template <int D, int B>
+__device__ __forceinline__ void unit_accumulate(const unsigned char* vbuf, int g, const uint32_t (&vread)[4],
+                                                const bf16x8 (&pf)[2], f32x16 (&oacc)[Tile<D, B>::NDT]) {
+  using T = Tile<D, B>;
 #pragma unroll
-  for (int i = 0; i < T::NDT; ++i)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-      oacc[i] = mfma32(*reinterpret_cast<const bf16x8*>(buf + T::KBYTES + vread[a] + i * 32 * T::VROW), pf[a],
-                       oacc[i]);
+    for (int i = 0; i < T::NDT; ++i)
+      oacc[i] = mfma32(*reinterpret_cast<const bf16x8*>(vbuf + vread[2 * g + b] + i * 32 * T::VROW), pf[b], oacc[i]);
+}
+
+// Workgroup barrier for the stage pipeline: wait until at most `NOut` of this lane's vector memory
+// operations (the LDS-direct copies) are outstanding and its LDS reads have returned, then s_barrier.
+// __syncthreads() would also wait for the copies still meant to be in flight.  As one volatile asm
+// statement with a memory clobber it is also a hard scheduling fence, so no LDS access moves across it
+// (the compiler does not model the LDS write of a direct copy).
+template <int NOut>
+__device__ __forceinline__ void block_sync() {
+  static_assert(NOut >= 0 && NOut < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0070 | NOut);  // vmcnt(NOut) lgkmcnt(0), visible to the compiler's scoreboard
+  asm volatile("s_barrier" ::: "memory");
 }
 
 template <int D, int B>
@@ -184,8 +241,13 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
     const int32_t* __restrict__ slot_of, const uint16_t* __restrict__ packed, int slot_capacity, float scale_log2,
     int Lq, int nb, int N, float* __restrict__ O, float* __restrict__ lse) {
   using T = Tile<D, B>;
-  __shared__ __align__(1024) unsigned char sStage0[T::STAGE];
-  __shared__ __align__(1024) unsigned char sStage1[T::STAGE];
+  // Separate double buffers for K and V^T.  The work is cut into units of 32 keys (two per stage); the
+  // scores of unit u + 1 are computed while unit u is turned into probabilities, and then unit u is
+  // accumulated, so K runs half a stage ahead of V.
+  __shared__ __align__(1024) unsigned char sK0[T::KBYTES];
+  __shared__ __align__(1024) unsigned char sK1[T::KBYTES];
+  __shared__ __align__(1024) unsigned char sV0[D * T::VROW];
+  __shared__ __align__(1024) unsigned char sV1[D * T::VROW];
   __shared__ int sList[kListCap];
   __shared__ int sWaveCnt[T::NW];
 
@@ -201,20 +263,21 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 #pragma unroll
   for (int f = 0; f < T::NQF; ++f) qf[f] = *reinterpret_cast<const bf16x8*>(Q + row * D + f * 16 + half * 8);
 
-  // This lane's LDS fragment addresses inside a stage buffer (swizzle key qr & 7 for every row it reads).
+  // This lane's LDS fragment addresses inside a buffer.  Every row it reads is qr plus a multiple of 32,
+  // so one swizzle key serves all of them.
   uint32_t kread[T::NQF], vread[4];
 #pragma unroll
-  for (int f = 0; f < T::NQF; ++f) kread[f] = qr * T::KROW + (((2 * f + half) ^ (qr & 7)) * 16);
+  for (int f = 0; f < T::NQF; ++f) kread[f] = qr * T::KROW + (((2 * f + half) ^ swizzle<T::KROW>(qr)) * 16);
 #pragma unroll
-  for (int a = 0; a < 4; ++a) vread[a] = qr * T::VROW + (((2 * a + half) ^ (qr & 7)) * 16);
+  for (int a = 0; a < 4; ++a) vread[a] = qr * T::VROW + (((2 * a + half) ^ swizzle<T::VROW>(qr)) * 16);
   CopyPlan<D, B> plan;
   plan.init(wave, lane);
 
-  f32x16 oacc[T::NDT];
+  RowState<D, B> rs;
 #pragma unroll
-  for (int i = 0; i < T::NDT; ++i) oacc[i] = f32x16{};
-  float m_run = -INFINITY;  // maximum the probabilities are taken against (log2-scaled logits)
-  float l_run = 0.f;        // sum of exp2(x - m_run) over this lane's keys
+  for (int i = 0; i < T::NDT; ++i) rs.oacc[i] = f32x16{};
+  rs.m_run = -INFINITY;
+  rs.l_run = 0.f;
 
   const uint8_t* mrow = mask + ((int64_t)h * Lq + k) * pitch;
   const int32_t* sof = slot_of + (int64_t)h * nb;
@@ -248,50 +311,77 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       __syncthreads();
     }
 
-    // Stages go to the two LDS buffers alternately; the loop body covers one stage in each so that
-    // every buffer access has a fixed base.
-    const int nstage = total * T::NST;
-    auto code_of = [&](int st) { return __builtin_amdgcn_readfirstlane(sList[st / T::NST]); };
-    auto lim_of = [&](int code, int st) {
-      return (code & 1) ? tail_valid - (st % T::NST) * kStageKeys - 8 * half : kStageKeys;
-    };
-    if (nstage > 0) plan.issue(pk + (int64_t)(code_of(0) >> 1) * T::SLOT_BYTES, 0, sStage0, wave);
-    for (int st = 0; st < nstage; st += 2) {
-      // even stage st in buffer 0
-      int code = code_of(st);
-      wait_vmem();
-      __syncthreads();  // stage st visible to all waves; buffer 1 no longer read (stage st - 1 done)
-      if (st + 1 < nstage) {
-        const int cn = code_of(st + 1);
-        plan.issue(pk + (int64_t)(cn >> 1) * T::SLOT_BYTES, (st + 1) % T::NST, sStage1, wave);
+    const int n = total * T::NST;  // stages of this pass
+    if (n > 0) {
+      // Slot code of stage s (clamped to the last stage: codes past the end are only read, never used).
+      auto code_of = [&](int s) { return __builtin_amdgcn_readfirstlane(sList[min(s, n - 1) / T::NST]); };
+      auto slot_ptr = [&](int code) { return pk + (int64_t)(code >> 1) * T::SLOT_BYTES; };
+      // Offset of the first padding key inside unit g of stage s, counted from 8 half (>= 32: none).
+      auto lim_of = [&](int code, int s, int g) {
+        return (code & 1) ? tail_valid - (s % T::NST) * kStageKeys - 32 * g - 8 * half : 32;
+      };
+
+      // One unit: head of its scores, then the next unit's scores beside its probabilities, then its
+      // accumulation.  After the last unit the "next" scores read a stale buffer and are dropped.
+      auto unit = [&](f32x16& cur, f32x16& nxt, const unsigned char* kbuf_next, int g_next,
+                      const unsigned char* vbuf, int g, int lim) {
+        bf16x8 pf[2];
+        unit_head<D, B>(cur, rs, scale_log2, lim);
+        nxt = unit_scores<D, B>(kbuf_next, g_next, kread, qf);
+        unit_probabilities(cur, scale_log2, rs.m_run, pf, rs.l_run);
+        unit_accumulate<D, B>(vbuf, g, vread, pf, rs.oacc);
+      };
+
+      // Copies: V^T[s + 1] is issued at the top of unit 2s (its buffer held V^T[s - 1], last read in unit
+      // 2s - 1), K[s + 2] at the top of unit 2s + 1 (its buffer held K[s], last read in unit 2s).  Each
+      // top waits for this lane's older copy and then for the whole workgroup, which makes V^T[s] (top of
+      // unit 2s) or K[s + 1] (top of unit 2s + 1) visible and frees the buffer it refills; the newer copy
+      // (CPT instructions) stays in flight when it was issued.
+      int c0 = code_of(0), c1 = code_of(1), c2 = code_of(2);  // codes of stages s, s + 1, s + 2
+      plan.issue_k(slot_ptr(c0), 0, sK0, wave);
+      plan.issue_v(slot_ptr(c0), 0, sV0, wave);
+      block_sync<0>();
+      if (n > 1) plan.issue_k(slot_ptr(c1), 1 % T::NST, sK1, wave);
+      f32x16 sa = unit_scores<D, B>(sK0, 0, kread, qf), sb;
+
+      for (int s = 0; s < n; s += 2) {
+        // stage s (even): K[s] in sK0, V^T[s] in sV0, K[s + 1] in sK1
+        if (s + 1 < n) block_sync<T::CPT>(); else block_sync<0>();
+        if (s + 1 < n) plan.issue_v(slot_ptr(c1), (s + 1) % T::NST, sV1, wave);
+        int c3 = code_of(s + 3);
+        unit(sa, sb, sK0, 1, sV0, 0, lim_of(c0, s, 0));
+        if (s + 1 < n) block_sync<T::CPT>(); else block_sync<0>();
+        if (s + 2 < n) plan.issue_k(slot_ptr(c2), (s + 2) % T::NST, sK0, wave);
+        unit(sb, sa, sK1, 0, sV0, 1, lim_of(c0, s, 1));
+        if (s + 1 >= n) break;
+        c0 = c1; c1 = c2; c2 = c3;
+
+        // stage s + 1 (odd): K[s + 1] in sK1, V^T[s + 1] in sV1, K[s + 2] in sK0
+        if (s + 2 < n) block_sync<T::CPT>(); else block_sync<0>();
+        if (s + 2 < n) plan.issue_v(slot_ptr(c1), (s + 2) % T::NST, sV0, wave);
+        c3 = code_of(s + 4);
+        unit(sa, sb, sK1, 1, sV1, 0, lim_of(c0, s + 1, 0));
+        if (s + 2 < n) block_sync<T::CPT>(); else block_sync<0>();
+        if (s + 3 < n) plan.issue_k(slot_ptr(c2), (s + 3) % T::NST, sK1, wave);
+        unit(sb, sa, sK0, 0, sV1, 1, lim_of(c0, s + 1, 1));
+        c0 = c1; c1 = c2; c2 = c3;
       }
-      stage_compute<D, B>(sStage0, kread, vread, qf, oacc, m_run, l_run, scale_log2, lim_of(code, st));
-      if (st + 1 >= nstage) break;
-      // odd stage st + 1 in buffer 1
-      code = code_of(st + 1);
-      wait_vmem();
-      __syncthreads();  // stage st + 1 visible; buffer 0 no longer read
-      if (st + 2 < nstage) {
-        const int cn = code_of(st + 2);
-        plan.issue(pk + (int64_t)(cn >> 1) * T::SLOT_BYTES, (st + 2) % T::NST, sStage0, wave);
-      }
-      stage_compute<D, B>(sStage1, kread, vread, qf, oacc, m_run, l_run, scale_log2, lim_of(code, st + 1));
     }
-    __syncthreads();  // sList and the stage buffers are reused by the next pass
+    __syncthreads();  // sList and the buffers are reused by the next pass
   }
 
-  const float l_tot = sum_halves(l_run);
+  const float l_tot = sum_halves(rs.l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   float* orow = O + row * D;
 #pragma unroll
   for (int i = 0; i < T::NDT; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float4 v = make_float4(oacc[i][4 * q + 0] * inv, oacc[i][4 * q + 1] * inv, oacc[i][4 * q + 2] * inv,
-                                   oacc[i][4 * q + 3] * inv);
+      const float4 v = make_float4(rs.oacc[i][4 * q + 0] * inv, rs.oacc[i][4 * q + 1] * inv,
+                                   rs.oacc[i][4 * q + 2] * inv, rs.oacc[i][4 * q + 3] * inv);
       *reinterpret_cast<float4*>(orow + i * 32 + q * 8 + half * 4) = v;
     }
-  if (half == 0) lse[row] = l_tot > 0.f ? m_run * 0.69314718055994531f + logf(l_tot) : -INFINITY;
+  if (half == 0) lse[row] = l_tot > 0.f ? rs.m_run * 0.69314718055994531f + logf(l_tot) : -INFINITY;
 }
 
 template <int D, int B>
