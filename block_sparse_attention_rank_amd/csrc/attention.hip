@@ -37,7 +37,6 @@ namespace sparsp {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((address_space(3))) const void lds_void;
 
@@ -79,7 +78,6 @@ __device__ __forceinline__ void copy16(const char* base, uint32_t voff, const un
 
 constexpr int kStageKeys = 64;     // keys per pipeline stage
 constexpr int kListCap = 512;      // selected blocks listed per pass over the mask row
-constexpr float kRescaleLog2 = 8.f;
 
 template <int D, int B>
 struct Tile {
@@ -162,12 +160,9 @@ __device__ __forceinline__ f32x16 unit_scores(const unsigned char* kbuf, int g, 
   return sacc;
 }
 
-// Prepare the scores of a unit for its probabilities: mask the padding keys of the last block (key
-// offsets at or past `lim` inside the unit, counted from 8 half) and raise the running maximum if some
-// row of the wave needs it.
-template <int D, int B>
-__device__ __forceinline__ void unit_head(f32x16& sacc, RowState<D, B>& rs, float scale_log2, int lim) {
-  using T = Tile<D, B>;
+// Mask the padding keys of the last block in a unit's scores: key offsets at or past `lim` inside the
+// unit, counted from 8 half (lim >= 24 masks nothing).
+__device__ __forceinline__ void unit_mask(f32x16& sacc, int lim) {
   if (lim < 32) {
 #pragma unroll
     for (int x = 0; x < 16; ++x) {
@@ -175,39 +170,24 @@ __device__ __forceinline__ void unit_head(f32x16& sacc, RowState<D, B>& rs, floa
       if (c >= lim) sacc[x] = -INFINITY;
     }
   }
-  float mx = -INFINITY;
-#pragma unroll
-  for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[x]);
-  mx *= scale_log2;  // scale_log2 > 0: the max commutes with scaling
-  if (__builtin_amdgcn_ballot_w64(mx > rs.m_run + kRescaleLog2) != 0) {
-    const float m_new = fmaxf(rs.m_run, max_halves(mx));
-    const float alpha = __builtin_amdgcn_exp2f(rs.m_run - m_new);
-    rs.m_run = m_new;
-    rs.l_run *= alpha;
-#pragma unroll
-    for (int i = 0; i < T::NDT; ++i) rs.oacc[i] *= alpha;
-  }
 }
 
-// Probabilities of a unit, rounded to bf16 for the second product; the row sum adds the same rounded
-// values (two per v_dot2 against (1, 1)).  pf[b] holds keys 16b + 8 half + 0..7 of the unit.
+// Probabilities of a unit, rounded to bf16 for the second product; the fp32 values are summed into
+// l_run (two add chains).  pf[b] holds keys 16b + 8 half + 0..7 of the unit.  (A v_dot2 against (1, 1)
+// would sum the rounded pairs in half the instructions, but on gfx950 it competes with the MFMAs of the
+// other wave on the SIMD and issues several times slower than two adds.)
 __device__ __forceinline__ void unit_probabilities(const f32x16& sacc, float scale_log2, float m_run, bf16x8 (&pf)[2],
                                                    float& l_run) {
-#pragma unroll
-  for (int x = 0; x < 16; ++x)
-    pf[x / 8][x % 8] = (__bf16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[x], scale_log2, -m_run));
-  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
   float l_odd = 0.f;
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const bf16x2 pair = {pf[b][e], pf[b][e + 1]};
-      if (e & 2)
-        l_odd = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_odd, false);
-      else
-        l_run = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, l_run, false);
-    }
+  for (int x = 0; x < 16; ++x) {
+    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[x], scale_log2, -m_run));
+    pf[x / 8][x % 8] = (__bf16)p;
+    if (x & 1)
+      l_odd += p;
+    else
+      l_run += p;
+  }
   l_run += l_odd;
 }
 
@@ -221,6 +201,34 @@ __device__ __forceinline__ void unit_accumulate(const unsigned char* vbuf, int g
 #pragma unroll
     for (int i = 0; i < T::NDT; ++i)
       oacc[i] = mfma32(*reinterpret_cast<const bf16x8*>(vbuf + vread[2 * g + b] + i * 32 * T::VROW), pf[b], oacc[i]);
+}
+
+// Probabilities of a unit relative to the running maximum, without a per-unit maximum: they may reach
+// 2^64 (exact in fp32 and bf16, and the fp32 sums stay far from overflow).  The lane's 16-key sum, which
+// the row sum needs anyway, tells whether any probability went past 2^64 (or is inf or NaN: the first
+// unit of a row, whose maximum is still -inf); only then is the maximum taken, the state rescaled and
+// the probabilities recomputed.
+template <int D, int B>
+__device__ __forceinline__ void unit_softmax(const f32x16& sacc, RowState<D, B>& rs, float scale_log2, bf16x8 (&pf)[2]) {
+  using T = Tile<D, B>;
+  float lu = 0.f;
+  unit_probabilities(sacc, scale_log2, rs.m_run, pf, lu);
+  if (__builtin_amdgcn_ballot_w64(!(lu < 0x1p64f)) != 0) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[x]);
+    const float m_new = fmaxf(rs.m_run, max_halves(mx * scale_log2));  // scale_log2 > 0
+    if (m_new != -INFINITY) {  // -inf: no key of the row seen yet; nothing to rescale
+      const float alpha = rs.m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rs.m_run - m_new);
+      rs.m_run = m_new;
+      rs.l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < T::NDT; ++i) rs.oacc[i] *= alpha;
+    }
+    lu = 0.f;
+    unit_probabilities(sacc, scale_log2, m_new == -INFINITY ? 0.f : m_new, pf, lu);
+  }
+  rs.l_run += lu;
 }
 
 // Workgroup barrier for the stage pipeline: wait until at most `NOut` of this lane's vector memory
@@ -326,9 +334,9 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       auto unit = [&](f32x16& cur, f32x16& nxt, const unsigned char* kbuf_next, int g_next,
                       const unsigned char* vbuf, int g, int lim) {
         bf16x8 pf[2];
-        unit_head<D, B>(cur, rs, scale_log2, lim);
+        unit_mask(cur, lim);
         nxt = unit_scores<D, B>(kbuf_next, g_next, kread, qf);
-        unit_probabilities(cur, scale_log2, rs.m_run, pf, rs.l_run);
+        unit_softmax<D, B>(cur, rs, scale_log2, pf);
         unit_accumulate<D, B>(vbuf, g, vread, pf, rs.oacc);
       };
 
