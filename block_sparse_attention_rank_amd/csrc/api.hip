@@ -6,7 +6,7 @@
 
 #include <string>
 
-#include "../../include/sparsp.h"
+#include "sparsp.h"
 #include "sparsp_internal.h"
 
 namespace {

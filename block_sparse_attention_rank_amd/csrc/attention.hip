@@ -24,11 +24,12 @@
 // any 8 consecutive rows apart.  Each lane's fragment addresses are fixed per kernel; the buffer, key
 // group and d tile are immediate offsets.
 //
-// Softmax.  The running maximum is only raised when some row of the wave grows by more than 2^8 (a
-// wave-uniform decision); until then probabilities are taken against the stale maximum, which is exact in
-// real arithmetic because numerator and denominator share it.  The common path therefore needs no
-// cross-lane step: the two halves of a row exchange their maxima (v_permlane32_swap) only when the
-// maximum moves, and their partial sums once at the end.
+// Softmax.  Probabilities are taken against a running maximum that is only raised when needed: they may
+// grow to 2^64 before the state is rescaled, which is exact in real arithmetic (numerator and
+// denominator share the maximum) and safe in fp32 and bf16.  A unit's row sums reveal when that bound
+// is passed (or a row has no maximum yet); only then is the unit's maximum taken, so the common path
+// has neither a maximum nor a cross-lane step: the two halves of a row exchange maxima
+// (v_permlane32_swap) only when the maximum moves, and their partial sums once at the end.
 #include <math.h>
 
 #include "sparsp_internal.h"
@@ -77,6 +78,7 @@ __device__ __forceinline__ void copy16(const char* base, uint32_t voff, const un
 }
 
 constexpr int kStageKeys = 64;     // keys per pipeline stage
+constexpr int kXcdChunk = 16;      // consecutive (head, query block) items kept on one XCD
 constexpr int kListCap = 512;      // selected blocks listed per pass over the mask row
 
 template <int D, int B>
@@ -247,7 +249,7 @@ template <int D, int B>
 __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) void bsa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint8_t* __restrict__ mask, int64_t pitch,
     const int32_t* __restrict__ slot_of, const uint16_t* __restrict__ packed, int slot_capacity, float scale_log2,
-    int Lq, int nb, int N, float* __restrict__ O, float* __restrict__ lse) {
+    int H, int Lq, int nb, int N, float* __restrict__ O, float* __restrict__ lse) {
   using T = Tile<D, B>;
   // Separate double buffers for K and V^T.  The work is cut into units of 32 keys (two per stage); the
   // scores of unit u + 1 are computed while unit u is turned into probabilities, and then unit u is
@@ -259,7 +261,8 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   __shared__ int sList[kListCap];
   __shared__ int sWaveCnt[T::NW];
 
-  const int wid = xcd_remap(blockIdx.x, gridDim.x);
+  const int wid = xcd_chunked<kXcdChunk>(blockIdx.x);
+  if (wid >= H * Lq) return;  // padding of the grid to whole chunk rounds
   const int h = wid / Lq, k = wid - h * Lq;
   const int t = threadIdx.x, lane = t % 64;
   const int wave = __builtin_amdgcn_readfirstlane(t / 64);
@@ -399,8 +402,10 @@ hipError_t launch_attention_t(const Dims& g, const uint16_t* Q, const uint8_t* m
   const int64_t items = (int64_t)g.H * g.Lq;
   if (items == 0) return hipSuccess;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipLaunchKernelGGL((bsa_fwd_kernel<D, B>), dim3((unsigned)items), dim3(2 * B), 0, stream, Q, mask, pitch,
-                     slot_of, packed, slot_capacity, scale_log2, g.Lq, g.nb, g.N, O, lse);
+  constexpr int64_t round = (int64_t)kXcds * kXcdChunk;
+  const int64_t grid = (items + round - 1) / round * round;
+  hipLaunchKernelGGL((bsa_fwd_kernel<D, B>), dim3((unsigned)grid), dim3(2 * B), 0, stream, Q, mask, pitch,
+                     slot_of, packed, slot_capacity, scale_log2, g.H, g.Lq, g.nb, g.N, O, lse);
   return hipGetLastError();
 }
 

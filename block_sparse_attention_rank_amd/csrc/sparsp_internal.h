@@ -37,6 +37,17 @@ hipError_t launch_attention(const Dims& g, const uint16_t* Q, const uint8_t* mas
 // XCDs round-robin, so kernels that want neighbouring work items to share an L2 remap their ids.
 constexpr int kXcds = 8;
 
+// Items dealt to the XCDs in chunks of `Chunk` consecutive items, cyclically: XCD x runs chunks x, x + 8,
+// x + 16, ... in order.  Neighbouring items (neighbouring query blocks of one head) stay on one XCD and
+// share its L2, while every XCD samples all heads, which balances heads of different cost.  Valid for a
+// grid of a multiple of 8 * Chunk workgroups; ids past the real item count are returned as they are
+// (callers skip them).
+template <int Chunk>
+__device__ __forceinline__ int xcd_chunked(int pid) {
+  const int xcd = pid % kXcds, idx = pid / kXcds;
+  return ((idx / Chunk) * kXcds + xcd) * Chunk + idx % Chunk;
+}
+
 __device__ __forceinline__ int xcd_remap(int pid, int total) {
   const int xcd = pid % kXcds, idx = pid / kXcds;
   const int base = total / kXcds, rem = total % kXcds;
