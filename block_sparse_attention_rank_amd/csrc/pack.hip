@@ -10,6 +10,24 @@ namespace sparsp {
 namespace {
 
 constexpr int kPackThreads = 256;
+constexpr bool kNtLoad = false;   // K and V are read once
+constexpr bool kNtStore = false;  // the packed buffer is written once
+
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+__device__ __forceinline__ u32x4 load16(const uint16_t* p) {
+  const u32x4* q = reinterpret_cast<const u32x4*>(p);
+  if (kNtLoad) return __builtin_nontemporal_load(q);
+  return *q;
+}
+
+__device__ __forceinline__ void store16(uint16_t* p, const u32x4& v) {
+  u32x4* q = reinterpret_cast<u32x4*>(p);
+  if (kNtStore)
+    __builtin_nontemporal_store(v, q);
+  else
+    *q = v;
+}
 
 // Transpose an 8 x 8 tile of 16-bit values held as 8 rows of 4 x 32-bit words (two values per word,
 // lower column in the low half).  Output row e holds input column e.
@@ -47,18 +65,18 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const uint16_t* __re
   uint16_t* dst = packed + (int64_t)s * kSlotElems;
 
   // K: a straight copy; consecutive threads move consecutive 16-byte chunks.
-  uint4 kv[kChunksPerThread];
+  u32x4 kv[kChunksPerThread];
 #pragma unroll
-  for (int i = 0; i < kChunksPerThread; ++i)
-    kv[i] = *reinterpret_cast<const uint4*>(K + src + (int64_t)(u + i * kSub) * 8);
+  for (int i = 0; i < kChunksPerThread; ++i) kv[i] = load16(K + src + (int64_t)(u + i * kSub) * 8);
 
-  // V: sub-tile (g, c) = keys 8g..8g+7, columns 8c..8c+7; consecutive threads take consecutive column
-  // chunks of the same rows, so the loads stay coalesced.
-  const int c = u % (D / 8), g = u / (D / 8);
+  // V: sub-tile (g, c) = keys 8g..8g+7, columns 8c..8c+7.  Consecutive threads take consecutive key
+  // groups g of the same column chunks, so each store instruction of a wave writes whole V^T rows
+  // (B keys) and every output line is written by one wave at once.
+  const int g = u % (B / 8), c = u / (B / 8);
   uint32_t vin[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint4 v = *reinterpret_cast<const uint4*>(V + src + (int64_t)(g * 8 + i) * D + c * 8);
+    const u32x4 v = load16(V + src + (int64_t)(g * 8 + i) * D + c * 8);
     vin[i][0] = v.x;
     vin[i][1] = v.y;
     vin[i][2] = v.z;
@@ -66,15 +84,16 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const uint16_t* __re
   }
 
 #pragma unroll
-  for (int i = 0; i < kChunksPerThread; ++i) *reinterpret_cast<uint4*>(dst + (int64_t)(u + i * kSub) * 8) = kv[i];
+  for (int i = 0; i < kChunksPerThread; ++i) store16(dst + (int64_t)(u + i * kSub) * 8, kv[i]);
 
   uint32_t vout[8][4];
   transpose8x8(vin, vout);
   uint16_t* vt = dst + (int64_t)B * D;
 #pragma unroll
-  for (int e = 0; e < 8; ++e)
-    *reinterpret_cast<uint4*>(vt + (int64_t)(c * 8 + e) * B + g * 8) =
-        make_uint4(vout[e][0], vout[e][1], vout[e][2], vout[e][3]);
+  for (int e = 0; e < 8; ++e) {
+    const u32x4 o = {vout[e][0], vout[e][1], vout[e][2], vout[e][3]};
+    store16(vt + (int64_t)(c * 8 + e) * B + g * 8, o);
+  }
 }
 
 template <int D, int B>
