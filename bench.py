@@ -196,6 +196,41 @@ def main():
     print(f"[bench] {w.name}: union {t_union * 1e3:.1f} us, pack {t_pack * 1e3:.1f} us, "
           f"attention {t_attn:.3f} ms, step {ms_per_step:.3f} ms", file=sys.stderr, flush=True)
 
+    # Segment-wise consumption: attention over each source rank's segment (local first, then ring
+    # distance 1, 2, ...) and the log-sum-exp merge of the partial results, as the payload would arrive.
+    ranges = bsa.segment_ranges(seg, g.H, g.G)
+    order = [(w.r + k) % w.G for k in range(w.G)]
+    parts = [(torch.empty_like(O), torch.empty_like(lse)) for _ in order]
+    accO, accL = torch.empty_like(O), torch.empty_like(lse)
+    seg_steps = max(3, args.steps // 4)
+
+    def seg_step(ev=None):
+        accO.zero_()
+        accL.fill_(float("-inf"))
+        for i, p in enumerate(order):
+            if ev is not None:
+                ev[2 * i].record(stream)
+            bsa.block_sparse_attn_segment(g, Q, mask, u.slot_of, packed, ranges[p][0], ranges[p][1], scale,
+                                          out=parts[i])
+            if ev is not None:
+                ev[2 * i + 1].record(stream)
+            bsa.merge_partial(g, accO, accL, *parts[i])
+        if ev is not None:
+            ev[2 * len(order)].record(stream)
+
+    seg_step()
+    torch.cuda.synchronize()
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(2 * len(order) + 1)] for _ in range(seg_steps)]
+    for i in range(seg_steps):
+        seg_step(sev[i])
+    torch.cuda.synchronize()
+    seg_total = float(np.mean([e[0].elapsed_time(e[-1]) for e in sev]))
+    seg_attn = float(np.mean([sum(e[2 * i].elapsed_time(e[2 * i + 1]) for i in range(len(order))) for e in sev]))
+    merge_ms = (seg_total - seg_attn) / max(1, len(order))
+    merge_bytes = (3 * O.numel() + 3 * lse.numel()) * 4  # read O, O_part, lse x2; write O, lse
+    print(f"[bench] {w.name}: segmented attention {seg_total:.3f} ms ({len(order)} segments), merge "
+          f"{merge_ms * 1e3:.1f} us each", file=sys.stderr, flush=True)
+
     attn_tflops = attn_flops / (t_attn * 1e-3) / 1e12
     pack_gbs = pack_bytes / (t_pack * 1e-3) / 1e9
     rec = {
@@ -227,6 +262,10 @@ def main():
             "attn_ms": round(t_attn, 4),
             "attn_TFLOPs": round(attn_tflops, 2),
             "attn_frac_bf16": round(attn_tflops / BF16_DENSE_TFLOPS, 4),
+            "segmented_attn_ms": round(seg_total, 4),
+            "segmented_attn_TFLOPs": round(attn_flops / (seg_total * 1e-3) / 1e12, 2),
+            "merge_us": round(merge_ms * 1e3, 2),
+            "merge_GBps": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1) if merge_ms > 0 else None,
         },
         "roofline": {
             "kernel": "bsa_fwd_kernel",

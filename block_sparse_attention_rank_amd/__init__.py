@@ -17,7 +17,8 @@ import numpy as np
 from ._lib import EXPORTS, LIB_PATH, Geometry, SparspError, check, load  # noqa: F401
 
 __all__ = ["Geometry", "SparspError", "UnionResult", "geometry", "local_query_blocks", "demand_union",
-           "pack_kv", "block_sparse_attn", "load", "LIB_PATH", "EXPORTS"]
+           "pack_kv", "block_sparse_attn", "block_sparse_attn_segment", "merge_partial", "segment_ranges", "load",
+           "LIB_PATH", "EXPORTS"]
 
 
 def geometry(H: int, d: int, b: int, N: int, G: int, r: int, Lq: int) -> Geometry:
@@ -133,3 +134,49 @@ def block_sparse_attn(g: Geometry, Q, mask, slot_of, packed, softmax_scale: floa
                                           _ptr(packed), packed.shape[0], scale, _ptr(O), _ptr(lse),
                                           _stream(stream)))
     return O, lse
+
+
+def _attn_outputs(g: Geometry, Q, out):
+    import torch
+    if out is None:
+        return (torch.empty((g.H, g.Lq * g.b, g.d), dtype=torch.float32, device=Q.device),
+                torch.empty((g.H, g.Lq * g.b), dtype=torch.float32, device=Q.device))
+    return out
+
+
+def block_sparse_attn_segment(g: Geometry, Q, mask, slot_of, packed, slot_lo: int, slot_hi: int,
+                              softmax_scale: float | None = None, out=None, stream=None):
+    """Attention over the selected blocks whose slot lies in [slot_lo, slot_hi)
+    (sparsp_block_sparse_attn_segment).  Returns the partial (O, lse)."""
+    import torch
+    _require(Q, "Q", torch.bfloat16, (g.H, g.Lq * g.b, g.d))
+    _require(mask, "mask", torch.uint8)
+    _require(slot_of, "slot_of", torch.int32, (g.H, g.nb))
+    _require(packed, "packed", torch.bfloat16)
+    if slot_hi > packed.shape[0]:
+        raise ValueError("packed holds fewer than slot_hi slots")
+    scale = 1.0 / math.sqrt(g.d) if softmax_scale is None else float(softmax_scale)
+    O, lse = _attn_outputs(g, Q, out)
+    check(load().sparsp_block_sparse_attn_segment(ctypes.byref(g), _ptr(Q), _ptr(mask), mask.shape[2],
+                                                  _ptr(slot_of), _ptr(packed), int(slot_lo), int(slot_hi), scale,
+                                                  _ptr(O), _ptr(lse), _stream(stream)))
+    return O, lse
+
+
+def merge_partial(g: Geometry, O, lse, O_part, lse_part, stream=None):
+    """Fold the partial result (O_part, lse_part) into (O, lse) in place (sparsp_merge_partial)."""
+    import torch
+    for t, name in ((O, "O"), (O_part, "O_part")):
+        _require(t, name, torch.float32, (g.H, g.Lq * g.b, g.d))
+    for t, name in ((lse, "lse"), (lse_part, "lse_part")):
+        _require(t, name, torch.float32, (g.H, g.Lq * g.b))
+    check(load().sparsp_merge_partial(ctypes.byref(g), _ptr(O), _ptr(lse), _ptr(O_part), _ptr(lse_part),
+                                      _stream(stream)))
+    return O, lse
+
+
+def segment_ranges(seg_offsets: np.ndarray, H: int, G: int) -> list[tuple[int, int]]:
+    """Slot range [lo, hi) of every source rank's segment, from the host copy of seg_offsets (each
+    source rank's heads are consecutive)."""
+    s = np.asarray(seg_offsets)
+    return [(int(s[p * H]), int(s[(p + 1) * H])) for p in range(G)]

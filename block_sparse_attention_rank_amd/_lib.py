@@ -25,6 +25,8 @@ EXPORTS = (
     "sparsp_demand_union",
     "sparsp_pack_kv",
     "sparsp_block_sparse_attn",
+    "sparsp_block_sparse_attn_segment",
+    "sparsp_merge_partial",
 )
 
 
@@ -76,6 +78,10 @@ def load() -> ctypes.CDLL:
     lib.sparsp_pack_kv.argtypes = [gp, P, P, P, P, P, i32, P, P]
     lib.sparsp_block_sparse_attn.restype = i32
     lib.sparsp_block_sparse_attn.argtypes = [gp, P, P, i64, P, P, i32, f32, P, P, P]
+    lib.sparsp_block_sparse_attn_segment.restype = i32
+    lib.sparsp_block_sparse_attn_segment.argtypes = [gp, P, P, i64, P, P, i32, i32, f32, P, P, P]
+    lib.sparsp_merge_partial.restype = i32
+    lib.sparsp_merge_partial.argtypes = [gp, P, P, P, P, P]
     _lib = lib
     return lib
 

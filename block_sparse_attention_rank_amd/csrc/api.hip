@@ -134,22 +134,58 @@ int32_t sparsp_pack_kv(const sparsp_geometry* geom, const uint16_t* K, const uin
                     fn);
 }
 
-int32_t sparsp_block_sparse_attn(const sparsp_geometry* geom, const uint16_t* Q, const uint8_t* mask,
-                                 int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed,
-                                 int32_t slot_capacity, float softmax_scale, float* O, float* lse, void* stream) {
-  static const char* fn = "sparsp_block_sparse_attn";
+namespace {
+
+// Shared checks and launch of the attention entry points over the slot range [slot_lo, slot_hi).
+int32_t attention_call(const char* fn, const sparsp_geometry* geom, const uint16_t* Q, const uint8_t* mask,
+                       int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed, int32_t slot_lo,
+                       int32_t slot_hi, float softmax_scale, float* O, float* lse, void* stream) {
   sparsp::Dims d;
   int32_t st = check_geometry(geom, fn, &d);
   if (st) return st;
   if ((st = check_mask(d, mask, mask_pitch, fn))) return st;
   if (d.Lq > 0 && (!Q || !slot_of || !packed || !O || !lse)) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
-  if (slot_capacity < 0) return fail(SPARSP_ERR_INVALID, fn, "slot_capacity must be >= 0");
   if (!isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(SPARSP_ERR_INVALID, fn, "softmax_scale must be finite and positive");
   if ((Q && !aligned16(Q)) || (packed && !aligned16(packed)) || (O && !aligned16(O)))
     return fail(SPARSP_ERR_INVALID, fn, "Q, packed and O must be 16-byte aligned");
-  return hip_status(sparsp::launch_attention(d, Q, mask, mask_pitch, slot_of, packed, slot_capacity, softmax_scale,
+  return hip_status(sparsp::launch_attention(d, Q, mask, mask_pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale,
                                              O, lse, reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // namespace
+
+int32_t sparsp_block_sparse_attn(const sparsp_geometry* geom, const uint16_t* Q, const uint8_t* mask,
+                                 int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed,
+                                 int32_t slot_capacity, float softmax_scale, float* O, float* lse, void* stream) {
+  static const char* fn = "sparsp_block_sparse_attn";
+  if (slot_capacity < 0) return fail(SPARSP_ERR_INVALID, fn, "slot_capacity must be >= 0");
+  return attention_call(fn, geom, Q, mask, mask_pitch, slot_of, packed, 0, slot_capacity, softmax_scale, O, lse,
+                        stream);
+}
+
+int32_t sparsp_block_sparse_attn_segment(const sparsp_geometry* geom, const uint16_t* Q, const uint8_t* mask,
+                                         int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed,
+                                         int32_t slot_lo, int32_t slot_hi, float softmax_scale, float* O, float* lse,
+                                         void* stream) {
+  static const char* fn = "sparsp_block_sparse_attn_segment";
+  if (slot_lo < 0 || slot_hi < slot_lo) return fail(SPARSP_ERR_INVALID, fn, "need 0 <= slot_lo <= slot_hi");
+  return attention_call(fn, geom, Q, mask, mask_pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse,
+                        stream);
+}
+
+int32_t sparsp_merge_partial(const sparsp_geometry* geom, float* O, float* lse, const float* O_part,
+                             const float* lse_part, void* stream) {
+  static const char* fn = "sparsp_merge_partial";
+  sparsp::Dims d;
+  int32_t st = check_geometry(geom, fn, &d);
+  if (st) return st;
+  if (d.Lq > 0 && (!O || !lse || !O_part || !lse_part)) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
+  if ((O && !aligned16(O)) || (O_part && !aligned16(O_part)))
+    return fail(SPARSP_ERR_INVALID, fn, "O and O_part must be 16-byte aligned");
+  const int64_t rows = (int64_t)d.H * d.Lq * d.b;
+  return hip_status(sparsp::launch_merge(rows, d.d, O, lse, O_part, lse_part, reinterpret_cast<hipStream_t>(stream)),
                     fn);
 }
 

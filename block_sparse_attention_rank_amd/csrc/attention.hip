@@ -248,7 +248,7 @@ __device__ __forceinline__ void block_sync() {
 template <int D, int B>
 __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) void bsa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint8_t* __restrict__ mask, int64_t pitch,
-    const int32_t* __restrict__ slot_of, const uint16_t* __restrict__ packed, int slot_capacity, float scale_log2,
+    const int32_t* __restrict__ slot_of, const uint16_t* __restrict__ packed, int slot_lo, int slot_hi, float scale_log2,
     int H, int Lq, int nb, int N, float* __restrict__ O, float* __restrict__ lse) {
   using T = Tile<D, B>;
   // Separate double buffers for K and V^T.  The work is cut into units of 32 keys (two per stage); the
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       int slot = -1;
       if (j < nb && mrow[j] != 0) {
         slot = sof[j];
-        if (slot >= slot_capacity) slot = -1;
+        if (slot < slot_lo || slot >= slot_hi) slot = -1;  // outside the consumed slot range
       }
       const uint64_t bal = __builtin_amdgcn_ballot_w64(slot >= 0);
       if (lane == 0) sWaveCnt[wave] = __popcll(bal);
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
 template <int D, int B>
 hipError_t launch_attention_t(const Dims& g, const uint16_t* Q, const uint8_t* mask, int64_t pitch,
-                              const int32_t* slot_of, const uint16_t* packed, int32_t slot_capacity,
+                              const int32_t* slot_of, const uint16_t* packed, int32_t slot_lo, int32_t slot_hi,
                               float softmax_scale, float* O, float* lse, hipStream_t stream) {
   const int64_t items = (int64_t)g.H * g.Lq;
   if (items == 0) return hipSuccess;
@@ -405,25 +405,25 @@ hipError_t launch_attention_t(const Dims& g, const uint16_t* Q, const uint8_t* m
   constexpr int64_t round = (int64_t)kXcds * kXcdChunk;
   const int64_t grid = (items + round - 1) / round * round;
   hipLaunchKernelGGL((bsa_fwd_kernel<D, B>), dim3((unsigned)grid), dim3(2 * B), 0, stream, Q, mask, pitch,
-                     slot_of, packed, slot_capacity, scale_log2, g.H, g.Lq, g.nb, g.N, O, lse);
+                     slot_of, packed, slot_lo, slot_hi, scale_log2, g.H, g.Lq, g.nb, g.N, O, lse);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attention(const Dims& g, const uint16_t* Q, const uint8_t* mask, int64_t pitch,
-                            const int32_t* slot_of, const uint16_t* packed, int32_t slot_capacity,
+                            const int32_t* slot_of, const uint16_t* packed, int32_t slot_lo, int32_t slot_hi,
                             float softmax_scale, float* O, float* lse, hipStream_t stream) {
   if (g.d == 128 && g.b == 128)
-    return launch_attention_t<128, 128>(g, Q, mask, pitch, slot_of, packed, slot_capacity, softmax_scale, O, lse,
+    return launch_attention_t<128, 128>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse,
                                         stream);
   if (g.d == 64 && g.b == 64)
-    return launch_attention_t<64, 64>(g, Q, mask, pitch, slot_of, packed, slot_capacity, softmax_scale, O, lse,
+    return launch_attention_t<64, 64>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse,
                                       stream);
   if (g.d == 128 && g.b == 64)
-    return launch_attention_t<128, 64>(g, Q, mask, pitch, slot_of, packed, slot_capacity, softmax_scale, O, lse,
+    return launch_attention_t<128, 64>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse,
                                        stream);
-  return launch_attention_t<64, 128>(g, Q, mask, pitch, slot_of, packed, slot_capacity, softmax_scale, O, lse,
+  return launch_attention_t<64, 128>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse,
                                      stream);
 }
 

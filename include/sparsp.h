@@ -19,6 +19,11 @@
  *   4. sparsp_block_sparse_attn   -- softmax(Q K^T / sqrt(d)) V (section 2.2) over the selected key
  *                                    blocks only, with an online softmax (section 2.3), reading K/V
  *                                    from the compacted buffer.
+ *   5. sparsp_block_sparse_attn_segment, sparsp_merge_partial
+ *                                 -- the same attention restricted to one range of packed slots (one
+ *                                    source rank's segment, consumed as it arrives: sections 5.1 and
+ *                                    7), and the log-sum-exp merge of such partial results (section
+ *                                    2.3's online softmax across pieces of KV).
  *
  * Conventions shared by every call
  *   - bf16 tensors are passed as uint16_t bit patterns (IEEE bfloat16).
@@ -45,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SPARSP_ABI_VERSION 1
+#define SPARSP_ABI_VERSION 2
 
 typedef enum sparsp_status {
   SPARSP_OK = 0,
@@ -149,6 +154,35 @@ int32_t sparsp_block_sparse_attn(const sparsp_geometry* g, const uint16_t* Q, co
                                  int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed,
                                  int32_t slot_capacity, float softmax_scale, float* O, float* lse,
                                  void* stream);
+
+/*
+ * Block-sparse attention over the selected blocks whose slot lies in [slot_lo, slot_hi) only (sections 2.3,
+ * 5.1 and 7: each source rank's segment of the payload is consumed as it arrives; segment p of rank r's
+ * payload is [seg_offsets[p*H], seg_offsets[(p+1)*H]) as written by sparsp_demand_union).  DEVICE pointers;
+ * arguments as for sparsp_block_sparse_attn, with packed holding at least slot_hi slots.
+ *   O, lse       the partial result over those keys: softmax-weighted mean of their V rows and the
+ *                log-sum-exp of their scaled logits; (0, -inf) for a row none of whose keys is in range
+ * Errors: as for sparsp_block_sparse_attn; SPARSP_ERR_INVALID also when slot_lo < 0 or slot_hi < slot_lo.
+ */
+int32_t sparsp_block_sparse_attn_segment(const sparsp_geometry* g, const uint16_t* Q, const uint8_t* mask,
+                                         int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed,
+                                         int32_t slot_lo, int32_t slot_hi, float softmax_scale, float* O,
+                                         float* lse, void* stream);
+
+/*
+ * Fold a partial attention result over one key set into a running result over a disjoint key set (section
+ * 2.3, online softmax across pieces of KV).  DEVICE pointers, rows = H * Lq * b of d floats:
+ *   O, lse            [H][Lq*b][d], [H][Lq*b] float32: the running result                (read, written)
+ *   O_part, lse_part  the partial result, e.g. from sparsp_block_sparse_attn_segment     (read)
+ * With m = max(lse, lse_part): lse <- m + ln(e^(lse - m) + e^(lse_part - m)) and
+ * O <- e^(lse_old - lse) O + e^(lse_part - lse) O_part; a row where both are -inf stays (0, -inf), so a
+ * running result may start as (0, -inf).  Merging every segment of the payload, in any order, gives the
+ * result of sparsp_block_sparse_attn up to rounding: each piece rounds its probabilities to bf16 relative
+ * to its own running maximum.
+ * Errors: SPARSP_ERR_INVALID (null pointers, O or O_part not 16-byte aligned); SPARSP_ERR_UNSUPPORTED (d).
+ */
+int32_t sparsp_merge_partial(const sparsp_geometry* g, float* O, float* lse, const float* O_part,
+                             const float* lse_part, void* stream);
 
 #ifdef __cplusplus
 }

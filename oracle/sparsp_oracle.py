@@ -249,3 +249,32 @@ def real_rows(q_blocks: np.ndarray, b: int, N: int) -> np.ndarray:
     """Boolean [Lq*b]: which local query rows are real tokens (< N)."""
     tok = (np.asarray(q_blocks, dtype=np.int64)[:, None] * b + np.arange(b)[None, :]).reshape(-1)
     return tok < N
+
+
+# --------------------------------------------------------------------------------------------------
+# segment-wise consumption (section 2.3 online softmax across pieces of KV; section 5.1 the payload of
+# each source rank arrives as its own piece)
+
+
+def attention_block_segment(Q, K, V, mask, placement, p: int, h: int, k: int, b: int, N: int, scale: float):
+    """O and lse of local query block k of head h over the keys of the selected blocks owned by rank p
+    only: the definition of attention restricted to that key set.  An empty set gives (0, -inf)."""
+    nb = -(-N // b)
+    row = np.array(mask[h, k, :nb], copy=True)
+    row[np.asarray(placement)[:nb] != p] = 0
+    toks = allowed_keys(row, nb, b, N)
+    q = bf16_to_f64(Q[h, k * b:(k + 1) * b])
+    O, lse, _ = _attend(q, bf16_to_f64(K[h, toks]), bf16_to_f64(V[h, toks]), scale)
+    return O, lse
+
+
+def lse_merge(O_a, lse_a, O_b, lse_b):
+    """Combine two partial results over disjoint key sets: the log-sum-exp of the union is
+    ln(e^lse_a + e^lse_b) and each part's weighted mean is weighted by its share e^(lse_part - lse).
+    Rows where both parts are empty stay (0, -inf)."""
+    lse_a, lse_b = np.asarray(lse_a, np.float64), np.asarray(lse_b, np.float64)
+    lse = np.logaddexp(lse_a, lse_b)
+    with np.errstate(invalid="ignore"):
+        wa = np.where(np.isfinite(lse), np.exp(lse_a - lse), 0.0)
+        wb = np.where(np.isfinite(lse), np.exp(lse_b - lse), 0.0)
+    return wa[..., None] * O_a + wb[..., None] * O_b, lse

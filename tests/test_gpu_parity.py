@@ -128,6 +128,10 @@ EDGE_CASES = {
     "k_offsets": custom(H=2, d=64, b=64, T=4, HW=512, G=2, r=1, k_offset_sigma=6.0, density=0.2),
     "many_ranks": custom(H=2, d=64, b=64, T=8, HW=1024, G=64, r=62, placement="periodic", density=0.1),
     "wide_row": custom(H=1, d=128, b=128, T=2, HW=128 * 150, G=2, r=1, density=0.45),
+    # per-block K offsets large enough that a row's logits jump by far more than 64 (log2 units) between
+    # key blocks, up and down: the running maximum must be raised (and exp2 would overflow) many times
+    "logit_jumps_d64": custom(H=2, d=64, b=64, T=4, HW=512, G=2, r=0, k_offset_sigma=40.0, density=0.3),
+    "logit_jumps_d128": custom(H=2, d=128, b=128, T=3, HW=640, G=2, r=1, k_offset_sigma=25.0, density=0.5),
 }
 
 
@@ -188,3 +192,61 @@ def test_repeat_runs_are_bit_identical(require_gpu):
     assert np.array_equal(to_host_u16(a["packed"][:S]), to_host_u16(b["packed"][:S]))
     assert np.array_equal(a["O"].cpu().numpy(), b["O"].cpu().numpy())
     assert np.array_equal(a["lse"].cpu().numpy(), b["lse"].cpu().numpy())
+
+
+SEGMENT_CASES = {
+    "small": None,
+    "seg_d128_periodic": custom(H=2, d=128, b=128, T=3, HW=1280, G=4, r=1, placement="periodic", density=0.4),
+    "seg_d64_ragged": custom(H=2, d=64, b=64, T=5, HW=200, G=3, r=2, density=0.5, k_offset_sigma=6.0),
+    "hunyuan": None,
+}
+
+
+@pytest.mark.parametrize("name", list(SEGMENT_CASES))
+def test_segments_and_merge(require_gpu, name):
+    """Attention over each source rank's segment of the payload, then the log-sum-exp merge in ring order
+    (the local segment first, then ring distance 1, 2, ...): every segment and the merged result match the
+    oracle, and the merged result matches the single pass."""
+    import torch
+    import block_sparse_attention_rank_amd as bsa
+    from _gpu import run_path
+    w = SEGMENT_CASES[name]
+    inp = _inputs(name) if w is None else make_inputs(w)
+    w = inp["workload"]
+    print(f"[parity] segments {name}", flush=True)
+    res = run_path(inp)
+    g, u = res["g"], res["union"]
+    dev = res["dev"]
+    ranges = bsa.segment_ranges(u.seg_offsets.cpu().numpy(), w.H, w.G)
+    Lq = len(inp["q_blocks"])
+    items = [(h, k) for h in range(w.H) for k in range(Lq)] if w.H * Lq <= 300 else _sample_items(inp, n_rand=3)
+    scale = 1.0 / math.sqrt(w.d)
+    acc_O = torch.zeros_like(res["O"])
+    acc_lse = torch.full_like(res["lse"], float("-inf"))
+    order = [(w.r + k) % w.G for k in range(w.G)]
+    for p in order:
+        lo, hi = ranges[p]
+        O_p, lse_p = bsa.block_sparse_attn_segment(g, dev["Q"], dev["mask"], u.slot_of, res["packed"], lo, hi, scale)
+        bsa.merge_partial(g, acc_O, acc_lse, O_p, lse_p)
+        torch.cuda.synchronize()
+        Od, ld = O_p.cpu().numpy(), lse_p.cpu().numpy()
+        errs = []
+        for h, k in items[:8]:
+            Oo, lo_ = O.attention_block_segment(inp["Q"], inp["K"], inp["V"], inp["mask"], inp["placement"], p, h, k,
+                                                w.b, w.N, scale)
+            rows = O.real_rows(inp["q_blocks"][k:k + 1], w.b, w.N)
+            errs.append(np.abs(Od[h, k * w.b:(k + 1) * w.b][rows] - Oo[rows]).ravel())
+            gl, ol = ld[h, k * w.b:(k + 1) * w.b][rows], lo_[rows]
+            assert np.array_equal(np.isfinite(gl), np.isfinite(ol))
+            fin = np.isfinite(ol)
+            if fin.any():
+                assert np.max(np.abs(gl[fin] - ol[fin]) / np.maximum(1.0, np.abs(ol[fin]))) <= 1e-3
+        e = np.concatenate(errs)
+        assert e.max() <= MAX_ABS and e.mean() <= MEAN_ABS, (p, e.max(), e.mean())
+    mx, mean = _check_attention(inp, acc_O.cpu().numpy(), acc_lse.cpu().numpy(), items)
+    real = O.real_rows(inp["q_blocks"], w.b, w.N)
+    d_single = np.abs(acc_O.cpu().numpy()[:, real] - res["O"].cpu().numpy()[:, real])
+    # both are within MAX_ABS of the exact result; they differ in where the probabilities were rounded to
+    # bf16 (relative to each piece's running maximum), so they agree to the sum of the two distances
+    assert d_single.max() <= 2 * MAX_ABS, d_single.max()
+    print(f"[parity] segments {name}: merged max {mx:.2e}, vs single pass {d_single.max():.2e}", flush=True)
