@@ -278,3 +278,43 @@ def lse_merge(O_a, lse_a, O_b, lse_b):
         wa = np.where(np.isfinite(lse), np.exp(lse_a - lse), 0.0)
         wb = np.where(np.isfinite(lse), np.exp(lse_b - lse), 0.0)
     return wa[..., None] * O_a + wb[..., None] * O_b, lse
+
+
+# --------------------------------------------------------------------------------------------------
+# placement permutation (section 4.3: the placement is realised as a fixed permutation of logical blocks
+# to (rank, offset) pairs, applied to the hidden states before the distributed region and undone after it)
+
+
+def placement_permutation(placement: np.ndarray, G: int) -> tuple[np.ndarray, np.ndarray]:
+    """Rank-major order of the logical blocks: rank 0's blocks first, then rank 1's, ...; inside a rank,
+    ascending logical index (the order of Q_p).  Returns pos int32 [nb] (the permuted position of logical
+    block j) and rank_offsets int32 [G+1] (rank p's blocks occupy [rank_offsets[p], rank_offsets[p+1])).
+    Written as the enumeration itself: a running counter over (p, j)."""
+    P = [int(x) for x in np.asarray(placement).tolist()]
+    nb = len(P)
+    pos = [-1] * nb
+    offsets = []
+    n = 0
+    for p in range(G):
+        offsets.append(n)
+        for j in range(nb):
+            if P[j] == p:
+                pos[j] = n
+                n += 1
+    offsets.append(n)
+    return np.array(pos, np.int32), np.array(offsets, np.int32)
+
+
+def permute_blocks(x: np.ndarray, pos: np.ndarray, b: int, inverse: bool = False) -> np.ndarray:
+    """Move whole blocks of b rows: x [outer][nb*b][C] -> y with y[o, pos[j]] = x[o, j] (forward) or
+    y[o, j] = x[o, pos[j]] (inverse).  Any dtype; the bytes are moved unchanged."""
+    outer, rows, C = x.shape
+    nb = rows // b
+    xb = x.reshape(outer, nb, b, C)
+    y = np.empty_like(xb)
+    for j in range(nb):
+        if inverse:
+            y[:, j] = xb[:, int(pos[j])]
+        else:
+            y[:, int(pos[j])] = xb[:, j]
+    return y.reshape(outer, rows, C)
