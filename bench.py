@@ -231,6 +231,33 @@ def main():
     print(f"[bench] {w.name}: segmented attention {seg_total:.3f} ms ({len(order)} segments), merge "
           f"{merge_ms * 1e3:.1f} us each", file=sys.stderr, flush=True)
 
+    # Placement permutation (section 4.3) of the layer's hidden states [nb*b][H*d] bf16 into rank-major
+    # block order and back: each call reads and writes every byte once.
+    pos, _ = bsa.placement_permutation(inp["placement"], g.G)
+    pos_d = torch.from_numpy(pos).cuda()
+    hidden = torch.randn((g.nb * g.b, g.H * g.d), device="cuda").to(torch.bfloat16)
+    hidden_p = torch.empty_like(hidden)
+    hidden_r = torch.empty_like(hidden)
+    for _ in range(2):
+        bsa.permute_blocks(hidden, pos_d, g.b, out=hidden_p)
+        bsa.permute_blocks(hidden_p, pos_d, g.b, inverse=True, out=hidden_r)
+    perm_steps = max(3, args.steps // 2)
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(perm_steps)]
+    for e in pev:
+        e[0].record(stream)
+        bsa.permute_blocks(hidden, pos_d, g.b, out=hidden_p)
+        e[1].record(stream)
+        bsa.permute_blocks(hidden_p, pos_d, g.b, inverse=True, out=hidden_r)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    assert torch.equal(hidden_r, hidden), "permutation round trip changed the hidden states"
+    t_perm = float(np.mean([e[0].elapsed_time(e[1]) for e in pev]))
+    t_iperm = float(np.mean([e[1].elapsed_time(e[2]) for e in pev]))
+    perm_bytes = 2 * hidden.numel() * hidden.element_size()
+    del hidden, hidden_p, hidden_r
+    print(f"[bench] {w.name}: permutation of hidden states {t_perm * 1e3:.1f} us, inverse {t_iperm * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+
     attn_tflops = attn_flops / (t_attn * 1e-3) / 1e12
     pack_gbs = pack_bytes / (t_pack * 1e-3) / 1e9
     rec = {
@@ -266,6 +293,11 @@ def main():
             "segmented_attn_TFLOPs": round(attn_flops / (seg_total * 1e-3) / 1e12, 2),
             "merge_us": round(merge_ms * 1e3, 2),
             "merge_GBps": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1) if merge_ms > 0 else None,
+            "permute_hidden_bytes": perm_bytes,
+            "permute_us": round(t_perm * 1e3, 2),
+            "permute_GBps": round(perm_bytes / (t_perm * 1e-3) / 1e9, 1),
+            "permute_inverse_us": round(t_iperm * 1e3, 2),
+            "permute_inverse_GBps": round(perm_bytes / (t_iperm * 1e-3) / 1e9, 1),
         },
         "roofline": {
             "kernel": "bsa_fwd_kernel",

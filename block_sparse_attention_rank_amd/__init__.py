@@ -17,8 +17,8 @@ import numpy as np
 from ._lib import EXPORTS, LIB_PATH, Geometry, SparspError, check, load  # noqa: F401
 
 __all__ = ["Geometry", "SparspError", "UnionResult", "geometry", "local_query_blocks", "demand_union",
-           "pack_kv", "block_sparse_attn", "block_sparse_attn_segment", "merge_partial", "segment_ranges", "load",
-           "LIB_PATH", "EXPORTS"]
+           "pack_kv", "block_sparse_attn", "block_sparse_attn_segment", "merge_partial", "segment_ranges",
+           "placement_permutation", "permute_blocks", "load", "LIB_PATH", "EXPORTS"]
 
 
 def geometry(H: int, d: int, b: int, N: int, G: int, r: int, Lq: int) -> Geometry:
@@ -180,3 +180,36 @@ def segment_ranges(seg_offsets: np.ndarray, H: int, G: int) -> list[tuple[int, i
     source rank's heads are consecutive)."""
     s = np.asarray(seg_offsets)
     return [(int(s[p * H]), int(s[(p + 1) * H])) for p in range(G)]
+
+
+def placement_permutation(placement: np.ndarray, G: int) -> tuple[np.ndarray, np.ndarray]:
+    """Rank-major block order (sparsp_placement_permutation, host call): returns pos int32 [nb] (the
+    permuted position of logical block j) and rank_offsets int32 [G+1]."""
+    P = np.ascontiguousarray(placement, dtype=np.int32)
+    pos = np.empty(len(P), dtype=np.int32)
+    offs = np.empty(G + 1, dtype=np.int32)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    check(load().sparsp_placement_permutation(P.ctypes.data_as(i32p), len(P), G, pos.ctypes.data_as(i32p),
+                                              offs.ctypes.data_as(i32p)))
+    return pos, offs
+
+
+def permute_blocks(x, pos, b: int, inverse: bool = False, out=None, stream=None):
+    """Move whole blocks of b rows of x [..., nb*b, C] (sparsp_permute_blocks): out[..., pos[j]] = x[..., j]
+    or, with ``inverse``, out[..., j] = x[..., pos[j]].  ``pos`` is a device int32 tensor [nb]."""
+    import torch
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or not x.is_contiguous() or x.dim() < 2:
+        raise ValueError("x must be a contiguous device tensor of at least 2 dimensions")
+    rows, C = x.shape[-2], x.shape[-1]
+    if rows % b:
+        raise ValueError("the row count must be a multiple of b")
+    nb = rows // b
+    _require(pos, "pos", torch.int32, (nb,))
+    outer = x.numel() // max(1, rows * C)
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
+        raise ValueError("out must match x")
+    check(load().sparsp_permute_blocks(_ptr(x), _ptr(out), outer, nb, b * C * x.element_size(), _ptr(pos),
+                                       1 if inverse else 0, _stream(stream)))
+    return out

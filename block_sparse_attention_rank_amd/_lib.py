@@ -27,6 +27,8 @@ EXPORTS = (
     "sparsp_block_sparse_attn",
     "sparsp_block_sparse_attn_segment",
     "sparsp_merge_partial",
+    "sparsp_placement_permutation",
+    "sparsp_permute_blocks",
 )
 
 
@@ -82,6 +84,10 @@ def load() -> ctypes.CDLL:
     lib.sparsp_block_sparse_attn_segment.argtypes = [gp, P, P, i64, P, P, i32, i32, f32, P, P, P]
     lib.sparsp_merge_partial.restype = i32
     lib.sparsp_merge_partial.argtypes = [gp, P, P, P, P, P]
+    lib.sparsp_placement_permutation.restype = i32
+    lib.sparsp_placement_permutation.argtypes = [i32p, i32, i32, i32p, i32p]
+    lib.sparsp_permute_blocks.restype = i32
+    lib.sparsp_permute_blocks.argtypes = [P, P, i64, i32, i64, P, i32, P]
     _lib = lib
     return lib
 

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <string>
+#include <vector>
 
 #include "sparsp.h"
 #include "sparsp_internal.h"
@@ -187,6 +188,41 @@ int32_t sparsp_merge_partial(const sparsp_geometry* geom, float* O, float* lse, 
   const int64_t rows = (int64_t)d.H * d.Lq * d.b;
   return hip_status(sparsp::launch_merge(rows, d.d, O, lse, O_part, lse_part, reinterpret_cast<hipStream_t>(stream)),
                     fn);
+}
+
+int32_t sparsp_placement_permutation(const int32_t* placement, int32_t nb, int32_t G, int32_t* pos,
+                                     int32_t* rank_offsets) {
+  static const char* fn = "sparsp_placement_permutation";
+  if (!placement || !pos || !rank_offsets) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
+  if (nb < 1 || G < 1) return fail(SPARSP_ERR_INVALID, fn, "nb and G must be >= 1");
+  for (int32_t j = 0; j < nb; ++j)
+    if (placement[j] < 0 || placement[j] >= G) return fail(SPARSP_ERR_INVALID, fn, "placement value outside [0, G)");
+  // Counting sort by rank: offsets are the exclusive prefix sums of the per-rank block counts, and a
+  // running cursor per rank keeps ascending logical order inside a rank.
+  std::vector<int32_t> cursor(G + 1, 0);
+  for (int32_t j = 0; j < nb; ++j) ++cursor[placement[j] + 1];
+  for (int32_t p = 0; p < G; ++p) cursor[p + 1] += cursor[p];
+  for (int32_t p = 0; p <= G; ++p) rank_offsets[p] = cursor[p];
+  for (int32_t j = 0; j < nb; ++j) pos[j] = cursor[placement[j]]++;
+  return SPARSP_OK;
+}
+
+int32_t sparsp_permute_blocks(const void* src, void* dst, int64_t outer, int32_t nb, int64_t block_bytes,
+                              const int32_t* pos, int32_t inverse, void* stream) {
+  static const char* fn = "sparsp_permute_blocks";
+  if (outer < 0) return fail(SPARSP_ERR_INVALID, fn, "outer must be >= 0");
+  if (nb < 1) return fail(SPARSP_ERR_INVALID, fn, "nb must be >= 1");
+  if (block_bytes < 16 || block_bytes % 16 != 0)
+    return fail(SPARSP_ERR_INVALID, fn, "block_bytes must be a positive multiple of 16");
+  if (outer == 0) return SPARSP_OK;
+  if (!src || !dst || !pos) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
+  if (!aligned16(src) || !aligned16(dst)) return fail(SPARSP_ERR_INVALID, fn, "src and dst must be 16-byte aligned");
+  if (src == dst) return fail(SPARSP_ERR_INVALID, fn, "src and dst must not overlap");
+  if (outer > (int64_t)0x7fffffff / nb) return fail(SPARSP_ERR_UNSUPPORTED, fn, "outer*nb must be < 2^31");
+  const hipError_t e = sparsp::launch_permute(src, dst, outer, nb, block_bytes, pos, inverse ? 1 : 0,
+                                              reinterpret_cast<hipStream_t>(stream));
+  if (e == hipErrorInvalidConfiguration) return fail(SPARSP_ERR_UNSUPPORTED, fn, "grid exceeds 2^31 - 1 workgroups");
+  return hip_status(e, fn);
 }
 
 }  // extern "C"

@@ -37,6 +37,10 @@ hipError_t launch_attention(const Dims& g, const uint16_t* Q, const uint8_t* mas
 hipError_t launch_merge(int64_t rows, int d, float* O, float* lse, const float* O_part, const float* lse_part,
                         hipStream_t stream);
 
+// Move whole blocks: dst[o][pos[j]] = src[o][j] (inverse = 0) or dst[o][j] = src[o][pos[j]] (inverse = 1).
+hipError_t launch_permute(const void* src, void* dst, int64_t outer, int nb, int64_t block_bytes, const int32_t* pos,
+                          int inverse, hipStream_t stream);
+
 // Number of XCDs whose L2 slices a launch is spread over (MI355X: 8).  Workgroup ids are handed to the
 // XCDs round-robin, so kernels that want neighbouring work items to share an L2 remap their ids.
 constexpr int kXcds = 8;

@@ -24,6 +24,10 @@
  *                                    source rank's segment, consumed as it arrives: sections 5.1 and
  *                                    7), and the log-sum-exp merge of such partial results (section
  *                                    2.3's online softmax across pieces of KV).
+ *   6. sparsp_placement_permutation, sparsp_permute_blocks
+ *                                 -- the placement realised as a permutation of whole blocks into
+ *                                    rank-major order, applied to hidden states and undone afterwards
+ *                                    (section 4.3).
  *
  * Conventions shared by every call
  *   - bf16 tensors are passed as uint16_t bit patterns (IEEE bfloat16).
@@ -50,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SPARSP_ABI_VERSION 2
+#define SPARSP_ABI_VERSION 3
 
 typedef enum sparsp_status {
   SPARSP_OK = 0,
@@ -183,6 +187,39 @@ int32_t sparsp_block_sparse_attn_segment(const sparsp_geometry* g, const uint16_
  */
 int32_t sparsp_merge_partial(const sparsp_geometry* g, float* O, float* lse, const float* O_part,
                              const float* lse_part, void* stream);
+
+/*
+ * The placement as a permutation of whole blocks (section 4.3: the placement is computed once per model
+ * geometry and SP degree as a deterministic map from logical blocks to (rank, offset) pairs).  HOST
+ * pointers.  Rank-major order: rank 0's blocks first, then rank 1's, ...; inside a rank, ascending logical
+ * index, so rank p's range of the permuted sequence holds Q_p in the order every other call uses.
+ *   placement     [nb] int32, P(j) in [0, G)                                               (read)
+ *   pos           [nb] int32: the permuted position of logical block j                    (written)
+ *   rank_offsets  [G + 1] int32: rank p's blocks occupy [rank_offsets[p], rank_offsets[p + 1]);
+ *                 rank_offsets[G] = nb                                                      (written)
+ * Errors: SPARSP_ERR_INVALID for null pointers, nb < 1, G < 1, or a placement value outside [0, G) (then
+ * nothing is written).
+ */
+int32_t sparsp_placement_permutation(const int32_t* placement, int32_t nb, int32_t G, int32_t* pos,
+                                     int32_t* rank_offsets);
+
+/*
+ * Apply the block permutation to a tensor (section 4.3: hidden states and position-dependent data are
+ * permuted before the distributed region; the inverse restores the original token order after it).
+ * DEVICE pointers.  The tensor is `outer` independent sequences of nb blocks of block_bytes bytes each
+ * (e.g. hidden states [nb*b][C] with outer = 1 and block_bytes = b*C*element size, or per-head
+ * [H][nb*b][d] with outer = H and block_bytes = b*d*element size).
+ *   src      [outer][nb][block_bytes]                                                      (read)
+ *   dst      [outer][nb][block_bytes]; must not overlap src                                (written)
+ *   pos      [nb] int32, a permutation of 0..nb-1 (from sparsp_placement_permutation)     (read)
+ *   inverse  0: dst[o][pos[j]] = src[o][j];  1: dst[o][j] = src[o][pos[j]]
+ * Bytes are moved unchanged.  A pos entry outside [0, nb) moves nothing for that block (its contents are
+ * not checked on the host).
+ * Errors: SPARSP_ERR_INVALID (null pointers, outer < 0, nb < 1, block_bytes not a positive multiple of 16,
+ * src or dst not 16-byte aligned, src == dst); SPARSP_ERR_UNSUPPORTED (more than 2^31 - 1 workgroups).
+ */
+int32_t sparsp_permute_blocks(const void* src, void* dst, int64_t outer, int32_t nb, int64_t block_bytes,
+                              const int32_t* pos, int32_t inverse, void* stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = bsa.load()
-    assert lib.sparsp_abi_version() == 2
+    assert lib.sparsp_abi_version() == 3
     assert lib.sparsp_status_string(0) == b"ok"
     assert lib.sparsp_status_string(1) == b"invalid argument"
     assert lib.sparsp_status_string(2) == b"unsupported configuration"
@@ -121,3 +121,39 @@ def test_compaction_lds_limit():
     pitch = 16384
     assert lib.sparsp_demand_union(ctypes.byref(g), FAKE, pitch, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                    None) == _lib.SPARSP_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("placement,G", [(placement_contiguous(929, 8), 8), (placement_periodic(929, 128, 3600, 8), 8),
+                                         (placement_periodic(3072, 64, 6144, 8), 8),
+                                         (np.random.default_rng(3).integers(0, 5, 200).astype(np.int32), 5),
+                                         (np.zeros(1, np.int32), 1)])
+def test_placement_permutation_matches_oracle(placement, G):
+    pos, offs = bsa.placement_permutation(placement, G)
+    opos, ooffs = O.placement_permutation(placement, G)
+    assert np.array_equal(pos, opos) and np.array_equal(offs, ooffs)
+
+
+def test_permutation_argument_checks():
+    lib = bsa.load()
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    E = _lib.SPARSP_ERR_INVALID
+    P = np.array([0, 1, 3], np.int32)
+    pos = np.full(3, -7, np.int32)
+    offs = np.zeros(4, np.int32)
+    assert lib.sparsp_placement_permutation(P.ctypes.data_as(i32p), 3, 3, pos.ctypes.data_as(i32p),
+                                            offs.ctypes.data_as(i32p)) == E
+    assert pos.tolist() == [-7, -7, -7]                 # nothing written on error
+    assert lib.sparsp_placement_permutation(None, 3, 3, pos.ctypes.data_as(i32p), offs.ctypes.data_as(i32p)) == E
+    assert lib.sparsp_placement_permutation(P.ctypes.data_as(i32p), 0, 3, pos.ctypes.data_as(i32p),
+                                            offs.ctypes.data_as(i32p)) == E
+    # device call: every case fails its check before a launch
+    assert lib.sparsp_permute_blocks(FAKE, FAKE + 4096, 1, 4, 24, FAKE, 0, None) == E      # not a multiple of 16
+    assert lib.sparsp_permute_blocks(FAKE, FAKE + 4096, 1, 4, 0, FAKE, 0, None) == E
+    assert lib.sparsp_permute_blocks(FAKE, FAKE + 4096, -1, 4, 32, FAKE, 0, None) == E
+    assert lib.sparsp_permute_blocks(FAKE, FAKE + 4096, 1, 0, 32, FAKE, 0, None) == E
+    assert lib.sparsp_permute_blocks(FAKE + 8, FAKE + 4096, 1, 4, 32, FAKE, 0, None) == E  # misaligned
+    assert lib.sparsp_permute_blocks(FAKE, FAKE, 1, 4, 32, FAKE, 0, None) == E             # in place
+    assert lib.sparsp_permute_blocks(None, FAKE, 1, 4, 32, FAKE, 0, None) == E
+    assert lib.sparsp_permute_blocks(FAKE, FAKE + 4096, 1, 4, 32, None, 0, None) == E
+    assert lib.sparsp_permute_blocks(FAKE, FAKE + 4096, 1 << 30, 4, 32, FAKE, 0, None) == _lib.SPARSP_ERR_UNSUPPORTED
+    assert lib.sparsp_permute_blocks(None, None, 0, 4, 32, None, 0, None) == _lib.SPARSP_OK  # empty: no launch
