@@ -318,3 +318,72 @@ def permute_blocks(x: np.ndarray, pos: np.ndarray, b: int, inverse: bool = False
         else:
             y[:, int(pos[j])] = xb[:, j]
     return y.reshape(outer, rows, C)
+
+
+# --------------------------------------------------------------------------------------------------
+# communication-volume accounting (section 3.1: volume a rank must receive; section 3.2 and Figure 4:
+# how widely a received block is shared by the rank's queries; section 3.3 and section 5.1 / Figure 9:
+# relayed ring traffic versus demand-directed delivery)
+
+
+def access_counts(mask: np.ndarray, nb: int) -> np.ndarray:
+    """cnt[h][j] = number of the rank's local query rows whose mask selects block j (int64 [H][nb]).
+    Written as the count itself: a loop over rows adding one per selected entry."""
+    H, Lq = mask.shape[0], mask.shape[1]
+    cnt = np.zeros((H, nb), dtype=np.int64)
+    for h in range(H):
+        for k in range(Lq):
+            cnt[h] += np.asarray(mask[h, k, :nb]) != 0
+    return cnt
+
+
+def ring_distance(p: int, c: int, G: int) -> int:
+    """Hops from producer p to consumer c along the ring p -> p+1 -> ... (section 2.3's Ring Attention)."""
+    return (c - p) % G
+
+
+def comm_volume(U_all: np.ndarray, placement: np.ndarray, G: int) -> dict:
+    """Block counts of three ways to deliver every consumer's demand (one block = one head's K and V of b
+    tokens).  U_all bool [G][H][nb]: consumer c's per-head demand union (Eq. 2 over c's own rows).
+
+    direct [G][G]   direct[c][p] = |{(h, j) : P(j) = p, U_c[h][j]}| for c != p, 0 on the diagonal: each
+                    selected block crosses one link, straight from its owner (section 5.1).
+    relay  [G][G]   relay[p][k] = blocks of producer p on ring hop k (from p+k-1 to p+k), k = 1..G-1:
+                    a block travels until its farthest consumer, each relay forwarding what ranks further
+                    downstream still need (section 3.3; Figure 9(a): the first hop carries everything the
+                    others selected); column 0 is 0.
+    dense  [G]      dense[p] = (G-1) * H * |{j : P(j) = p}|: the whole shard of every head on every hop.
+    """
+    G_, H, nb = U_all.shape
+    assert G_ == G
+    P = [int(x) for x in np.asarray(placement).tolist()]
+    direct = np.zeros((G, G), dtype=np.int64)
+    relay = np.zeros((G, G), dtype=np.int64)
+    dense = np.zeros(G, dtype=np.int64)
+    for p in range(G):
+        dense[p] = (G - 1) * H * sum(1 for j in range(nb) if P[j] == p)
+    for h in range(H):
+        for j in range(nb):
+            p = P[j]
+            far = 0
+            for c in range(G):
+                if c != p and U_all[c, h, j]:
+                    direct[c, p] += 1
+                    far = max(far, ring_distance(p, c, G))
+            for k in range(1, far + 1):
+                relay[p, k] += 1
+    return dict(direct=direct, relay=relay, dense=dense)
+
+
+def sharing_fractions(cnt: np.ndarray, placement: np.ndarray, r: int, Lq: int) -> np.ndarray:
+    """Figure 4's quantity for rank r: for every remote block (h, j) the rank receives (P(j) != r and some
+    local row selects it), the fraction of the rank's local query blocks that access it.  Returns the
+    fractions as a float64 array (one entry per received remote block, in (h, j) order)."""
+    P = np.asarray(placement)
+    out = []
+    H, nb = cnt.shape
+    for h in range(H):
+        for j in range(nb):
+            if P[j] != r and cnt[h, j] > 0:
+                out.append(cnt[h, j] / Lq)
+    return np.array(out, dtype=np.float64)
