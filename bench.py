@@ -38,6 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="hunyuan")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-comm", action="store_true", help="skip the communication-volume accounting")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle attention sample")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the warmup, run one plain float32 device copy of this many MiB (read + write of "
@@ -112,6 +113,66 @@ def cpu_baseline(inp, budget_s: float, pairs: int, attn_flops: float):
                    f"{t_attn_full:.0f} s; value = all tiles' FLOPs / ({t_union:.2f} + {t_pack:.2f} + "
                    f"{t_attn_full:.0f}) s"),
         "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def comm_accounting(w, inp, g, torch, bsa):
+    """Communication volume of the workload's masks, every logical row drawn, for G = 2, 4, 8 under the
+    contiguous and the periodic placement: blocks moved by demand-directed delivery, by a relaying ring
+    and by a dense ring (sections 3.1, 3.3 and 5.1), from the GPU's demand unions of every rank's rows.
+    Also the Figure 4 sharing metric of this rank's received remote blocks."""
+    import dataclasses
+
+    import numpy as np
+    from workloads.configs import make_mask, placement_for
+
+    mask_all = make_mask(w, np.arange(w.nb, dtype=np.int32))
+    dev_all = torch.from_numpy(mask_all).cuda()
+    slot_bytes = 2 * w.b * w.d * 2
+    table = []
+    for placement in ("contiguous", "periodic"):
+        for G in (2, 4, 8):
+            wg = dataclasses.replace(w, G=G, placement=placement, r=0)
+            P = placement_for(wg)
+            Pd = torch.from_numpy(P).cuda()
+            words = []
+            for c in range(G):
+                q = np.flatnonzero(P == c)
+                gc = bsa.geometry(H=w.H, d=w.d, b=w.b, N=w.N, G=G, r=c, Lq=len(q))
+                rows = dev_all[:, torch.from_numpy(q).cuda(), :].contiguous()
+                words.append(bsa.demand_union(gc, rows, Pd).demand.cpu().numpy().view(np.uint64))
+            v = bsa.comm_volume(np.stack(words), P, G)
+            n = np.bincount(P, minlength=G)
+            remote_dense = int(sum(w.H * (w.nb - n[c]) for c in range(G)))
+            direct, relay, dense = int(v["direct"].sum()), int(v["relay"].sum()), int(v["dense"].sum())
+            table.append({
+                "placement": placement, "G": G,
+                "direct_blocks": direct, "relay_block_hops": relay, "dense_ring_block_hops": dense,
+                "direct_GB": round(direct * slot_bytes / 1e9, 3), "relay_GB": round(relay * slot_bytes / 1e9, 3),
+                "dense_ring_GB": round(dense * slot_bytes / 1e9, 3),
+                "reduction_vs_all_remote": round(1 - direct / remote_dense, 4) if remote_dense else None,
+                "relay_over_direct": round(relay / direct, 3) if direct else None,
+            })
+    # Figure 4: how many of this rank's local query blocks use each remote block it receives
+    Lq = len(inp["q_blocks"])
+    mask_d = torch.from_numpy(inp["mask"]).cuda()
+    cnt = bsa.demand_counts(g, mask_d)
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    evs[0].record()
+    for _ in range(10):
+        bsa.demand_counts(g, mask_d, out=cnt)
+    evs[1].record()
+    torch.cuda.synchronize()
+    c = cnt.cpu().numpy()
+    remote = (inp["placement"][None, :] != w.r) & (c > 0)
+    frac = c[remote] / max(1, Lq)
+    return {
+        "placements": table,
+        "sharing_rank_r": {"remote_blocks": int(remote.sum()),
+                           "used_by_ge_10pct": round(float((frac >= 0.10).mean()), 4) if frac.size else None,
+                           "used_by_ge_30pct": round(float((frac >= 0.30).mean()), 4) if frac.size else None},
+        "counts_kernel_us": round(evs[0].elapsed_time(evs[1]) * 100, 2),
     }
 
 
@@ -258,6 +319,13 @@ def main():
     print(f"[bench] {w.name}: permutation of hidden states {t_perm * 1e3:.1f} us, inverse {t_iperm * 1e3:.1f} us",
           file=sys.stderr, flush=True)
 
+    comm = None
+    if not args.no_comm and g.nb <= 1024:
+        t0 = time.perf_counter()
+        comm = comm_accounting(w, inp, g, torch, bsa)
+        print(f"[bench] {w.name}: communication accounting took {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+              flush=True)
+
     attn_tflops = attn_flops / (t_attn * 1e-3) / 1e12
     pack_gbs = pack_bytes / (t_pack * 1e-3) / 1e9
     rec = {
@@ -317,6 +385,7 @@ def main():
             "frac": round(pack_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("pack", w.name),
         },
+        "comm_volume": comm,
         "sources_digest": kernel_sources_digest(),
     }
     if not args.no_cpu:

@@ -18,7 +18,7 @@ from ._lib import EXPORTS, LIB_PATH, Geometry, SparspError, check, load  # noqa:
 
 __all__ = ["Geometry", "SparspError", "UnionResult", "geometry", "local_query_blocks", "demand_union",
            "pack_kv", "block_sparse_attn", "block_sparse_attn_segment", "merge_partial", "segment_ranges",
-           "placement_permutation", "permute_blocks", "load", "LIB_PATH", "EXPORTS"]
+           "placement_permutation", "permute_blocks", "demand_counts", "comm_volume", "load", "LIB_PATH", "EXPORTS"]
 
 
 def geometry(H: int, d: int, b: int, N: int, G: int, r: int, Lq: int) -> Geometry:
@@ -213,3 +213,37 @@ def permute_blocks(x, pos, b: int, inverse: bool = False, out=None, stream=None)
     check(load().sparsp_permute_blocks(_ptr(x), _ptr(out), outer, nb, b * C * x.element_size(), _ptr(pos),
                                        1 if inverse else 0, _stream(stream)))
     return out
+
+
+def demand_counts(g: Geometry, mask, out=None, stream=None):
+    """Access counts of the rank's mask rows (sparsp_demand_counts): int32 [H][nb], the number of local
+    query blocks selecting each key block."""
+    import torch
+    _require(mask, "mask", torch.uint8)
+    if mask.dim() != 3 or mask.shape[0] != g.H or mask.shape[1] != g.Lq:
+        raise ValueError("mask must be [H][Lq][pitch]")
+    if out is None:
+        out = torch.empty((g.H, g.nb), dtype=torch.int32, device=mask.device)
+    else:
+        _require(out, "counts", torch.int32, (g.H, g.nb))
+    check(load().sparsp_demand_counts(ctypes.byref(g), _ptr(mask), mask.shape[2], _ptr(out), _stream(stream)))
+    return out
+
+
+def comm_volume(demand_all: np.ndarray, placement: np.ndarray, G: int) -> dict:
+    """Block counts of demand-directed delivery, the relaying ring and the dense ring (sparsp_comm_volume,
+    host call).  demand_all: uint64 (or int64) [G][H][W], consumer c's demand words."""
+    D = np.ascontiguousarray(demand_all).view(np.uint64)
+    if D.ndim != 3 or D.shape[0] != G:
+        raise ValueError("demand_all must be [G][H][W]")
+    P = np.ascontiguousarray(placement, dtype=np.int32)
+    H, W = D.shape[1], D.shape[2]
+    if W != -(-len(P) // 64):
+        raise ValueError("demand words do not match the placement length")
+    direct = np.empty((G, G), np.int64)
+    relay = np.empty((G, G), np.int64)
+    dense = np.empty(G, np.int64)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    check(load().sparsp_comm_volume(D.ctypes.data, G, H, len(P), P.ctypes.data_as(i32p), direct.ctypes.data,
+                                    relay.ctypes.data, dense.ctypes.data))
+    return dict(direct=direct, relay=relay, dense=dense)

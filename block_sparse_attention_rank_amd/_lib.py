@@ -29,6 +29,8 @@ EXPORTS = (
     "sparsp_merge_partial",
     "sparsp_placement_permutation",
     "sparsp_permute_blocks",
+    "sparsp_demand_counts",
+    "sparsp_comm_volume",
 )
 
 
@@ -88,6 +90,10 @@ def load() -> ctypes.CDLL:
     lib.sparsp_placement_permutation.argtypes = [i32p, i32, i32, i32p, i32p]
     lib.sparsp_permute_blocks.restype = i32
     lib.sparsp_permute_blocks.argtypes = [P, P, i64, i32, i64, P, i32, P]
+    lib.sparsp_demand_counts.restype = i32
+    lib.sparsp_demand_counts.argtypes = [gp, P, i64, P, P]
+    lib.sparsp_comm_volume.restype = i32
+    lib.sparsp_comm_volume.argtypes = [P, i32, i32, i32, i32p, P, P, P]
     _lib = lib
     return lib
 

@@ -225,4 +225,47 @@ int32_t sparsp_permute_blocks(const void* src, void* dst, int64_t outer, int32_t
   return hip_status(e, fn);
 }
 
+int32_t sparsp_demand_counts(const sparsp_geometry* geom, const uint8_t* mask, int64_t mask_pitch, int32_t* counts,
+                             void* stream) {
+  static const char* fn = "sparsp_demand_counts";
+  sparsp::Dims d;
+  int32_t st = check_geometry(geom, fn, &d);
+  if (st) return st;
+  if ((st = check_mask(d, mask, mask_pitch, fn))) return st;
+  if (!counts) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
+  return hip_status(sparsp::launch_counts(d, mask, mask_pitch, counts, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t sparsp_comm_volume(const uint64_t* demand, int32_t G, int32_t H, int32_t nb, const int32_t* placement,
+                           int64_t* direct, int64_t* relay, int64_t* dense) {
+  static const char* fn = "sparsp_comm_volume";
+  if (!demand || !placement || !direct || !relay || !dense) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
+  if (G < 1 || G > sparsp::kMaxRanks) return fail(SPARSP_ERR_INVALID, fn, "G must lie in [1, 64]");
+  if (H < 1 || nb < 1) return fail(SPARSP_ERR_INVALID, fn, "H and nb must be >= 1");
+  for (int32_t j = 0; j < nb; ++j)
+    if (placement[j] < 0 || placement[j] >= G) return fail(SPARSP_ERR_INVALID, fn, "placement value outside [0, G)");
+  const int64_t W = (nb + 63) / 64;
+  std::vector<int64_t> dir((size_t)G * G, 0), rel((size_t)G * G, 0), den(G, 0);
+  for (int32_t j = 0; j < nb; ++j) den[placement[j]] += (int64_t)(G - 1) * H;
+  for (int32_t h = 0; h < H; ++h)
+    for (int32_t j = 0; j < nb; ++j) {
+      const int32_t p = placement[j];
+      int32_t far = 0;  // ring distance of the farthest consumer of (h, j)
+      for (int32_t c = 0; c < G; ++c) {
+        if (c == p) continue;
+        const uint64_t word = demand[((int64_t)c * H + h) * W + j / 64];
+        if ((word >> (j % 64)) & 1u) {
+          ++dir[(size_t)c * G + p];
+          const int32_t dist = (c - p + G) % G;
+          if (dist > far) far = dist;
+        }
+      }
+      for (int32_t k = 1; k <= far; ++k) ++rel[(size_t)p * G + k];
+    }
+  memcpy(direct, dir.data(), dir.size() * sizeof(int64_t));
+  memcpy(relay, rel.data(), rel.size() * sizeof(int64_t));
+  memcpy(dense, den.data(), den.size() * sizeof(int64_t));
+  return SPARSP_OK;
+}
+
 }  // extern "C"

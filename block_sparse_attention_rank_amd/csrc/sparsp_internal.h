@@ -37,6 +37,9 @@ hipError_t launch_attention(const Dims& g, const uint16_t* Q, const uint8_t* mas
 hipError_t launch_merge(int64_t rows, int d, float* O, float* lse, const float* O_part, const float* lse_part,
                         hipStream_t stream);
 
+// cnt[h][j] = number of the rank's mask rows of head h that select block j.
+hipError_t launch_counts(const Dims& g, const uint8_t* mask, int64_t pitch, int32_t* counts, hipStream_t stream);
+
 // Move whole blocks: dst[o][pos[j]] = src[o][j] (inverse = 0) or dst[o][j] = src[o][pos[j]] (inverse = 1).
 hipError_t launch_permute(const void* src, void* dst, int64_t outer, int nb, int64_t block_bytes, const int32_t* pos,
                           int inverse, hipStream_t stream);

@@ -28,6 +28,11 @@
  *                                 -- the placement realised as a permutation of whole blocks into
  *                                    rank-major order, applied to hidden states and undone afterwards
  *                                    (section 4.3).
+ *   7. sparsp_demand_counts, sparsp_comm_volume
+ *                                 -- communication-volume accounting: how many local query blocks share
+ *                                    each demanded block (section 3.2, Figure 4), and the blocks that
+ *                                    demand-directed delivery, a relaying ring and a dense ring move
+ *                                    (sections 3.1, 3.3 and 5.1, Figure 9).
  *
  * Conventions shared by every call
  *   - bf16 tensors are passed as uint16_t bit patterns (IEEE bfloat16).
@@ -54,7 +59,7 @@
 extern "C" {
 #endif
 
-#define SPARSP_ABI_VERSION 3
+#define SPARSP_ABI_VERSION 4
 
 typedef enum sparsp_status {
   SPARSP_OK = 0,
@@ -220,6 +225,36 @@ int32_t sparsp_placement_permutation(const int32_t* placement, int32_t nb, int32
  */
 int32_t sparsp_permute_blocks(const void* src, void* dst, int64_t outer, int32_t nb, int64_t block_bytes,
                               const int32_t* pos, int32_t inverse, void* stream);
+
+/*
+ * Access counts of the rank's mask rows (section 3.2 and Figure 4: the share of a rank's query blocks that
+ * use each KV block it receives).  DEVICE pointers.
+ *   mask     as for sparsp_demand_union                                                    (read)
+ *   counts   [H][nb] int32: number of local rows k with mask[h][k][j] != 0                 (written)
+ * counts > 0 is the demand union of sparsp_demand_union.  Deterministic, integer-only.
+ * Errors: as for sparsp_demand_union's geometry and mask checks; SPARSP_ERR_INVALID for a NULL counts.
+ */
+int32_t sparsp_demand_counts(const sparsp_geometry* g, const uint8_t* mask, int64_t mask_pitch, int32_t* counts,
+                             void* stream);
+
+/*
+ * Communication volume of delivering every rank's demand, in blocks (one block = one head's K and V of b
+ * tokens; multiply by 2*b*d*element size for bytes).  HOST pointers.  Sections 3.1 and 3.3, section 5.1 and
+ * Figure 9.
+ *   demand     [G][H][W] uint64: demand[c] is consumer c's union as written by sparsp_demand_union for
+ *              geometry r = c (bits >= nb are ignored)                                      (read)
+ *   placement  [nb] int32, P(j) in [0, G)                                                   (read)
+ *   direct     [G][G] int64: direct[c][p] = blocks of producer p that consumer c demands, c != p; the
+ *              diagonal is 0 (demand-directed delivery: each block crosses one link once)  (written)
+ *   relay      [G][G] int64: relay[p][k] = blocks of producer p on ring hop k (from rank p+k-1 to p+k),
+ *              k = 1..G-1, when each rank passes on what ranks further along still demand; column 0 is 0
+ *                                                                                            (written)
+ *   dense      [G] int64: (G-1)*H*|{j : P(j) = p}|, the whole shard on every hop            (written)
+ * Errors: SPARSP_ERR_INVALID for null pointers, G outside [1, 64], H < 1, nb < 1, or a placement value
+ * outside [0, G) (then nothing is written).
+ */
+int32_t sparsp_comm_volume(const uint64_t* demand, int32_t G, int32_t H, int32_t nb, const int32_t* placement,
+                           int64_t* direct, int64_t* relay, int64_t* dense);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = bsa.load()
-    assert lib.sparsp_abi_version() == 3
+    assert lib.sparsp_abi_version() == 4
     assert lib.sparsp_status_string(0) == b"ok"
     assert lib.sparsp_status_string(1) == b"invalid argument"
     assert lib.sparsp_status_string(2) == b"unsupported configuration"
@@ -157,3 +157,45 @@ def test_permutation_argument_checks():
     assert lib.sparsp_permute_blocks(FAKE, FAKE + 4096, 1, 4, 32, None, 0, None) == E
     assert lib.sparsp_permute_blocks(FAKE, FAKE + 4096, 1 << 30, 4, 32, FAKE, 0, None) == _lib.SPARSP_ERR_UNSUPPORTED
     assert lib.sparsp_permute_blocks(None, None, 0, 4, 32, None, 0, None) == _lib.SPARSP_OK  # empty: no launch
+
+
+def _unions_all(mask_all, P, G, nb):
+    U = np.zeros((G, mask_all.shape[0], nb), dtype=bool)
+    for c in range(G):
+        U[c] = O.demand_union(mask_all[:, O.local_query_blocks(P, c), :], nb)
+    return U
+
+
+@pytest.mark.parametrize("H,nb,G,p,seed", [(1, 16, 4, 0.2, 0), (3, 130, 8, 0.05, 1), (2, 64, 5, 0.5, 2),
+                                           (2, 65, 1, 0.3, 3), (4, 200, 16, 0.02, 4)])
+def test_comm_volume_matches_oracle(H, nb, G, p, seed):
+    """The host accounting call against the oracle's loops, on demand words the oracle built."""
+    rng = np.random.default_rng(seed)
+    P = rng.integers(0, G, nb).astype(np.int32)
+    mask_all = np.zeros((H, nb, 64 * (-(-nb // 64))), np.uint8)
+    mask_all[:, :, :nb] = rng.random((H, nb, nb)) < p
+    U = _unions_all(mask_all, P, G, nb)
+    words = np.stack([O.demand_words(U[c]) for c in range(G)])
+    got = bsa.comm_volume(words, P, G)
+    want = O.comm_volume(U, P, G)
+    for key in ("direct", "relay", "dense"):
+        assert np.array_equal(got[key], want[key]), key
+
+
+def test_accounting_argument_checks():
+    lib = bsa.load()
+    E = _lib.SPARSP_ERR_INVALID
+    g = _geom()
+    assert lib.sparsp_demand_counts(ctypes.byref(g), FAKE, 64, None, None) == E
+    assert lib.sparsp_demand_counts(ctypes.byref(g), FAKE, 8, FAKE, None) == E          # pitch < nb
+    assert lib.sparsp_demand_counts(ctypes.byref(_geom(d=96)), FAKE, 64, FAKE, None) == _lib.SPARSP_ERR_UNSUPPORTED
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    P = np.array([0, 1, 2], np.int32)
+    words = np.zeros((2, 1, 1), np.uint64)
+    out = np.zeros(64, np.int64)
+    args = (words.ctypes.data, 2, 1, 3, P.ctypes.data_as(i32p), out.ctypes.data, out.ctypes.data, out.ctypes.data)
+    assert lib.sparsp_comm_volume(*args) == E                                            # P = 2 outside [0, 2)
+    assert b"placement" in lib.sparsp_last_error()
+    assert lib.sparsp_comm_volume(None, *args[1:]) == E
+    assert lib.sparsp_comm_volume(words.ctypes.data, 65, 1, 3, P.ctypes.data_as(i32p), out.ctypes.data,
+                                  out.ctypes.data, out.ctypes.data) == E
