@@ -387,3 +387,64 @@ def sharing_fractions(cnt: np.ndarray, placement: np.ndarray, r: int, Lq: int) -
             if P[j] != r and cnt[h, j] > 0:
                 out.append(cnt[h, j] / Lq)
     return np.array(out, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------------------------------
+# mask materialisation from pooled tiles (section 4.2: block-sparse video DiT kernels build their block
+# mask from pooled query and key tiles before the attention kernel runs; the evaluation uses CDF
+# thresholds, and the Top-p rule with a Top-k safety floor comes from the FVAttn abstract on the pages)
+
+
+def pool_blocks(X: np.ndarray, b: int, N: int, block_ids=None) -> np.ndarray:
+    """Mean of the real token rows of every block: X uint16 (bf16 bits) [H][n*b][d] -> float64 [H][n][d].
+    Block k covers rows k*b .. k*b+b-1 of X and is logical block block_ids[k] (default k), whose real
+    tokens are those with index < N; padded rows are not counted."""
+    H, rows, d = X.shape
+    n = rows // b
+    ids = np.arange(n) if block_ids is None else np.asarray(block_ids)
+    x = bf16_to_f64(X)
+    out = np.zeros((H, n, d))
+    for k in range(n):
+        real = min(b, N - int(ids[k]) * b)
+        if real > 0:
+            out[:, k] = x[:, k * b:k * b + real].sum(axis=1) / real
+    return out
+
+
+def block_scores(q_pooled: np.ndarray, k_pooled: np.ndarray, scale: float) -> np.ndarray:
+    """s[h][k][j] = scale * <q_pooled[h][k], k_pooled[h][j]> (the block-level QK^T)."""
+    return np.einsum("hkc,hjc->hkj", q_pooled, k_pooled) * scale
+
+
+def select_row(scores: np.ndarray, tau: float, k_min: int) -> tuple[list, int]:
+    """Top-p selection with a Top-k floor for one row of block scores.
+
+    Blocks in descending score order (equal scores: ascending j); p_j = exp(s_j - max s) / Z; n_tau =
+    the smallest n >= 1 whose first n blocks carry at least tau of the mass; n = min(nb, max(k_min,
+    n_tau)).  Returns (the order, n): the selected blocks are order[:n]."""
+    nb = len(scores)
+    order = sorted(range(nb), key=lambda j: (-float(scores[j]), j))
+    m = max(float(x) for x in scores)
+    p = [np.exp(float(scores[j]) - m) for j in order]
+    Z = float(sum(p))
+    cum, n_tau = 0.0, nb
+    for i in range(nb):
+        cum += p[i]
+        if cum >= tau * Z:
+            n_tau = i + 1
+            break
+    return order, min(nb, max(k_min, n_tau))
+
+
+def materialize_mask(q_pooled: np.ndarray, k_pooled: np.ndarray, scale: float, tau: float, k_min: int,
+                     pitch: int) -> np.ndarray:
+    """uint8 mask [H][Lq][pitch] (columns >= nb are 0) from pooled tiles: every row's selected blocks."""
+    H, Lq, _ = q_pooled.shape
+    nb = k_pooled.shape[1]
+    s = block_scores(q_pooled, k_pooled, scale)
+    mask = np.zeros((H, Lq, pitch), np.uint8)
+    for h in range(H):
+        for k in range(Lq):
+            order, n = select_row(s[h, k], tau, k_min)
+            mask[h, k, order[:n]] = 1
+    return mask
