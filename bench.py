@@ -319,6 +319,34 @@ def main():
     print(f"[bench] {w.name}: permutation of hidden states {t_perm * 1e3:.1f} us, inverse {t_iperm * 1e3:.1f} us",
           file=sys.stderr, flush=True)
 
+    # Mask materialisation from pooled tiles (section 4.2): pool K (every block) and the local Q blocks,
+    # then score and select every local row (Top-p 0.9 with a Top-k floor of 16 blocks).
+    mat = None
+    if g.nb <= 4096:
+        ids_d = torch.from_numpy(inp["q_blocks"]).cuda()
+        kp = bsa.pool_blocks(g, K)
+        qp = bsa.pool_blocks(g, Q, block_ids=ids_d)
+        mat_mask = bsa.materialize_mask(g, qp, kp, 0.9, 16)
+        mev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(max(3, args.steps // 2))]
+        for e in mev:
+            e[0].record(stream)
+            bsa.pool_blocks(g, K, out=kp)
+            e[1].record(stream)
+            bsa.pool_blocks(g, Q, block_ids=ids_d, out=qp)
+            e[2].record(stream)
+            bsa.materialize_mask(g, qp, kp, 0.9, 16, out=mat_mask)
+            e[3].record(stream)
+        torch.cuda.synchronize()
+        t_pk, t_pq, t_sel = (float(np.mean([e[i].elapsed_time(e[i + 1]) for e in mev])) for i in range(3))
+        k_bytes = K.numel() * 2 * w.N // (g.nb * g.b)          # real rows of K are read
+        mat = {"pool_k_us": round(t_pk * 1e3, 2), "pool_k_GBps": round(k_bytes / (t_pk * 1e-3) / 1e9, 1),
+               "pool_q_us": round(t_pq * 1e3, 2), "select_us": round(t_sel * 1e3, 2),
+               "tau": 0.9, "k_min": 16,
+               "density": round(float(mat_mask[:, :, :g.nb].float().mean().item()), 4)}
+        del kp, qp, mat_mask
+        print(f"[bench] {w.name}: mask materialisation: pool K {t_pk * 1e3:.1f} us, pool Q {t_pq * 1e3:.1f} us, "
+              f"select {t_sel * 1e3:.1f} us", file=sys.stderr, flush=True)
+
     comm = None
     if not args.no_comm and g.nb <= 1024:
         t0 = time.perf_counter()
@@ -386,6 +414,7 @@ def main():
             "traffic": measured_traffic("pack", w.name),
         },
         "comm_volume": comm,
+        "mask_materialisation": mat,
         "sources_digest": kernel_sources_digest(),
     }
     if not args.no_cpu:

@@ -18,7 +18,8 @@ from ._lib import EXPORTS, LIB_PATH, Geometry, SparspError, check, load  # noqa:
 
 __all__ = ["Geometry", "SparspError", "UnionResult", "geometry", "local_query_blocks", "demand_union",
            "pack_kv", "block_sparse_attn", "block_sparse_attn_segment", "merge_partial", "segment_ranges",
-           "placement_permutation", "permute_blocks", "demand_counts", "comm_volume", "load", "LIB_PATH", "EXPORTS"]
+           "placement_permutation", "permute_blocks", "demand_counts", "comm_volume", "pool_blocks",
+           "materialize_mask", "load", "LIB_PATH", "EXPORTS"]
 
 
 def geometry(H: int, d: int, b: int, N: int, G: int, r: int, Lq: int) -> Geometry:
@@ -247,3 +248,38 @@ def comm_volume(demand_all: np.ndarray, placement: np.ndarray, G: int) -> dict:
     check(load().sparsp_comm_volume(D.ctypes.data, G, H, len(P), P.ctypes.data_as(i32p), direct.ctypes.data,
                                     relay.ctypes.data, dense.ctypes.data))
     return dict(direct=direct, relay=relay, dense=dense)
+
+
+def pool_blocks(g: Geometry, X, block_ids=None, out=None, stream=None):
+    """Block means of the real rows (sparsp_pool_blocks): X bf16 [H][n*b][d] -> float32 [H][n][d].
+    ``block_ids`` (device int32 [n]) names each block's logical id; None means block k is block k."""
+    import torch
+    _require(X, "X", torch.bfloat16)
+    if X.dim() != 3 or X.shape[0] != g.H or X.shape[2] != g.d or X.shape[1] % g.b:
+        raise ValueError("X must be [H][n*b][d]")
+    n = X.shape[1] // g.b
+    if block_ids is not None:
+        _require(block_ids, "block_ids", torch.int32, (n,))
+    if out is None:
+        out = torch.empty((g.H, n, g.d), dtype=torch.float32, device=X.device)
+    else:
+        _require(out, "pooled", torch.float32, (g.H, n, g.d))
+    check(load().sparsp_pool_blocks(ctypes.byref(g), _ptr(X), n, _ptr(block_ids), _ptr(out), _stream(stream)))
+    return out
+
+
+def materialize_mask(g: Geometry, q_pooled, k_pooled, tau: float, k_min: int, softmax_scale: float | None = None,
+                     out=None, stream=None):
+    """Block mask [H][Lq][64*W] uint8 of the rank's rows from pooled tiles (sparsp_materialize_mask):
+    Top-p at CDF threshold ``tau`` with a Top-k floor ``k_min``."""
+    import torch
+    _require(q_pooled, "q_pooled", torch.float32, (g.H, g.Lq, g.d))
+    _require(k_pooled, "k_pooled", torch.float32, (g.H, g.nb, g.d))
+    scale = 1.0 / math.sqrt(g.d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((g.H, g.Lq, 64 * g.W), dtype=torch.uint8, device=q_pooled.device)
+    else:
+        _require(out, "mask", torch.uint8)
+    check(load().sparsp_materialize_mask(ctypes.byref(g), _ptr(q_pooled), _ptr(k_pooled), scale, float(tau),
+                                         int(k_min), _ptr(out), out.shape[2], _stream(stream)))
+    return out

@@ -31,6 +31,8 @@ EXPORTS = (
     "sparsp_permute_blocks",
     "sparsp_demand_counts",
     "sparsp_comm_volume",
+    "sparsp_pool_blocks",
+    "sparsp_materialize_mask",
 )
 
 
@@ -94,6 +96,10 @@ def load() -> ctypes.CDLL:
     lib.sparsp_demand_counts.argtypes = [gp, P, i64, P, P]
     lib.sparsp_comm_volume.restype = i32
     lib.sparsp_comm_volume.argtypes = [P, i32, i32, i32, i32p, P, P, P]
+    lib.sparsp_pool_blocks.restype = i32
+    lib.sparsp_pool_blocks.argtypes = [gp, P, i32, P, P, P]
+    lib.sparsp_materialize_mask.restype = i32
+    lib.sparsp_materialize_mask.argtypes = [gp, P, P, f32, f32, i32, P, i64, P]
     _lib = lib
     return lib
 

@@ -268,4 +268,43 @@ int32_t sparsp_comm_volume(const uint64_t* demand, int32_t G, int32_t H, int32_t
   return SPARSP_OK;
 }
 
+int32_t sparsp_pool_blocks(const sparsp_geometry* geom, const uint16_t* X, int32_t n_blocks, const int32_t* block_ids,
+                           float* pooled, void* stream) {
+  static const char* fn = "sparsp_pool_blocks";
+  sparsp::Dims d;
+  int32_t st = check_geometry(geom, fn, &d);
+  if (st) return st;
+  if (n_blocks < 0 || n_blocks > d.nb) return fail(SPARSP_ERR_INVALID, fn, "n_blocks must lie in [0, nb]");
+  if (d.H > 65535) return fail(SPARSP_ERR_UNSUPPORTED, fn, "H must be <= 65535");
+  if (n_blocks == 0) return SPARSP_OK;
+  if (!X || !pooled) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
+  if (!aligned16(X) || !aligned16(pooled)) return fail(SPARSP_ERR_INVALID, fn, "X and pooled must be 16-byte aligned");
+  return hip_status(sparsp::launch_pool(d, X, n_blocks, block_ids, pooled, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+int32_t sparsp_materialize_mask(const sparsp_geometry* geom, const float* q_pooled, const float* k_pooled,
+                                float softmax_scale, float tau, int32_t k_min, uint8_t* mask, int64_t mask_pitch,
+                                void* stream) {
+  static const char* fn = "sparsp_materialize_mask";
+  sparsp::Dims d;
+  int32_t st = check_geometry(geom, fn, &d);
+  if (st) return st;
+  if ((st = check_mask(d, mask, mask_pitch, fn))) return st;
+  if (d.nb > sparsp::kMaxSelectBlocks) return fail(SPARSP_ERR_UNSUPPORTED, fn, "nb must be <= 4096");
+  if (d.H > 65535) return fail(SPARSP_ERR_UNSUPPORTED, fn, "H must be <= 65535");
+  if (!(tau >= 0.f && tau <= 1.f)) return fail(SPARSP_ERR_INVALID, fn, "tau must lie in [0, 1]");
+  if (k_min < 0) return fail(SPARSP_ERR_INVALID, fn, "k_min must be >= 0");
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.f))
+    return fail(SPARSP_ERR_INVALID, fn, "softmax_scale must be finite and positive");
+  if (d.Lq == 0) return SPARSP_OK;
+  if (!q_pooled || !k_pooled) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
+  if (!aligned16(q_pooled) || !aligned16(k_pooled))
+    return fail(SPARSP_ERR_INVALID, fn, "q_pooled and k_pooled must be 16-byte aligned");
+  if (mask_pitch > 16384 || sparsp::select_lds_bytes(d.nb, d.d, mask_pitch) > 65536)
+    return fail(SPARSP_ERR_UNSUPPORTED, fn, "mask_pitch too large for one workgroup's LDS");
+  return hip_status(sparsp::launch_select(d, q_pooled, k_pooled, softmax_scale, tau, k_min, mask, mask_pitch,
+                                          reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

@@ -40,6 +40,16 @@ hipError_t launch_merge(int64_t rows, int d, float* O, float* lse, const float* 
 // cnt[h][j] = number of the rank's mask rows of head h that select block j.
 hipError_t launch_counts(const Dims& g, const uint8_t* mask, int64_t pitch, int32_t* counts, hipStream_t stream);
 
+// Block means of the real rows: X [H][n_blocks*b][d] bf16 -> pooled [H][n_blocks][d] fp32; block k is logical
+// block block_ids[k] (k when block_ids is null).
+hipError_t launch_pool(const Dims& g, const uint16_t* X, int n_blocks, const int32_t* block_ids, float* pooled,
+                       hipStream_t stream);
+// Mask rows [H][Lq][pitch] from pooled tiles: Top-p (tau) with a Top-k floor (k_min) over the block scores.
+hipError_t launch_select(const Dims& g, const float* q_pooled, const float* k_pooled, float scale, float tau,
+                         int k_min, uint8_t* mask, int64_t pitch, hipStream_t stream);
+size_t select_lds_bytes(int nb, int d, int64_t pitch);
+constexpr int kMaxSelectBlocks = 4096;
+
 // Move whole blocks: dst[o][pos[j]] = src[o][j] (inverse = 0) or dst[o][j] = src[o][pos[j]] (inverse = 1).
 hipError_t launch_permute(const void* src, void* dst, int64_t outer, int nb, int64_t block_bytes, const int32_t* pos,
                           int inverse, hipStream_t stream);

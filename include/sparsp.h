@@ -33,6 +33,10 @@
  *                                    each demanded block (section 3.2, Figure 4), and the blocks that
  *                                    demand-directed delivery, a relaying ring and a dense ring move
  *                                    (sections 3.1, 3.3 and 5.1, Figure 9).
+ *   8. sparsp_pool_blocks, sparsp_materialize_mask
+ *                                 -- the block mask itself, built from pooled query and key tiles
+ *                                    (section 4.2): block means, block scores, and per row a Top-p
+ *                                    (CDF threshold) selection with a Top-k floor.
  *
  * Conventions shared by every call
  *   - bf16 tensors are passed as uint16_t bit patterns (IEEE bfloat16).
@@ -59,7 +63,7 @@
 extern "C" {
 #endif
 
-#define SPARSP_ABI_VERSION 4
+#define SPARSP_ABI_VERSION 5
 
 typedef enum sparsp_status {
   SPARSP_OK = 0,
@@ -255,6 +259,43 @@ int32_t sparsp_demand_counts(const sparsp_geometry* g, const uint8_t* mask, int6
  */
 int32_t sparsp_comm_volume(const uint64_t* demand, int32_t G, int32_t H, int32_t nb, const int32_t* placement,
                            int64_t* direct, int64_t* relay, int64_t* dense);
+
+/*
+ * Block-mean pooling (section 4.2: masks are materialised from pooled query and key tiles).  DEVICE
+ * pointers.
+ *   X          [H][n_blocks*b][d] bf16: n_blocks blocks of b token rows per head         (read)
+ *   block_ids  [n_blocks] int32: logical block id of block k, which fixes its real rows (tokens < N);
+ *              NULL means block k is logical block k (all of K: n_blocks = nb; for the local queries
+ *              pass q_blocks)                                                              (read)
+ *   pooled     [H][n_blocks][d] float32: mean of the block's real rows, 0 if it has none   (written)
+ * Rows at token index >= N are not read.  Sums are fp32 in a fixed order (deterministic).
+ * Errors: SPARSP_ERR_INVALID (null pointers, n_blocks outside [0, nb], X or pooled not 16-byte aligned);
+ * SPARSP_ERR_UNSUPPORTED (d or b outside {64, 128}, H > 65535).
+ */
+int32_t sparsp_pool_blocks(const sparsp_geometry* g, const uint16_t* X, int32_t n_blocks, const int32_t* block_ids,
+                           float* pooled, void* stream);
+
+/*
+ * Block mask of the rank's rows from pooled tiles (section 4.2).  DEVICE pointers.
+ *   q_pooled   [H][Lq][d] float32: pooled local query blocks (sparsp_pool_blocks over Q)   (read)
+ *   k_pooled   [H][nb][d] float32: pooled key blocks (sparsp_pool_blocks over K)           (read)
+ *   softmax_scale  multiplies the pooled dot products (1/sqrt(d)); finite, > 0
+ *   tau        CDF threshold in [0, 1]
+ *   k_min      Top-k floor, >= 0
+ *   mask       [H][Lq][mask_pitch] uint8, the format sparsp_demand_union and sparsp_block_sparse_attn
+ *              read: 1 for a selected block, 0 elsewhere, columns >= nb included         (written)
+ * Row k of head h: scores s_j = softmax_scale * <q_pooled[h][k], k_pooled[h][j]>; blocks in descending
+ * score order (equal scores: ascending j); weights exp(s_j - max s); the first n blocks are selected,
+ * n = min(nb, max(k_min, n_tau)) with n_tau the shortest prefix holding at least tau of the total weight.
+ * Arithmetic is fp32: a block whose score or prefix weight sits within rounding of the decision may
+ * fall either way.
+ * Errors: SPARSP_ERR_INVALID (null pointers, bad pitch or alignment, tau outside [0, 1], k_min < 0, a
+ * scale that is not finite and > 0); SPARSP_ERR_UNSUPPORTED (d or b outside {64, 128}, nb > 4096,
+ * H > 65535).
+ */
+int32_t sparsp_materialize_mask(const sparsp_geometry* g, const float* q_pooled, const float* k_pooled,
+                                float softmax_scale, float tau, int32_t k_min, uint8_t* mask, int64_t mask_pitch,
+                                void* stream);
 
 #ifdef __cplusplus
 }

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = bsa.load()
-    assert lib.sparsp_abi_version() == 4
+    assert lib.sparsp_abi_version() == 5
     assert lib.sparsp_status_string(0) == b"ok"
     assert lib.sparsp_status_string(1) == b"invalid argument"
     assert lib.sparsp_status_string(2) == b"unsupported configuration"
@@ -199,3 +199,27 @@ def test_accounting_argument_checks():
     assert lib.sparsp_comm_volume(None, *args[1:]) == E
     assert lib.sparsp_comm_volume(words.ctypes.data, 65, 1, 3, P.ctypes.data_as(i32p), out.ctypes.data,
                                   out.ctypes.data, out.ctypes.data) == E
+
+
+def test_materialize_argument_checks():
+    lib = bsa.load()
+    E, U = _lib.SPARSP_ERR_INVALID, _lib.SPARSP_ERR_UNSUPPORTED
+    g = _geom()
+    gp = ctypes.byref(g)
+    assert lib.sparsp_pool_blocks(gp, FAKE, 9, None, FAKE, None) == E                 # n_blocks > nb = 8
+    assert lib.sparsp_pool_blocks(gp, FAKE, -1, None, FAKE, None) == E
+    assert lib.sparsp_pool_blocks(gp, None, 2, None, FAKE, None) == E
+    assert lib.sparsp_pool_blocks(gp, FAKE + 4, 2, None, FAKE, None) == E              # misaligned
+    assert lib.sparsp_pool_blocks(gp, None, 0, None, None, None) == _lib.SPARSP_OK      # nothing to do
+    assert lib.sparsp_pool_blocks(ctypes.byref(_geom(H=70000, Lq=1)), FAKE, 2, None, FAKE, None) == U
+    mm = lib.sparsp_materialize_mask
+    assert mm(gp, FAKE, FAKE, 0.1, 1.5, 0, FAKE, 64, None) == E                          # tau > 1
+    assert mm(gp, FAKE, FAKE, 0.1, -0.1, 0, FAKE, 64, None) == E
+    assert mm(gp, FAKE, FAKE, 0.1, float("nan"), 0, FAKE, 64, None) == E
+    assert mm(gp, FAKE, FAKE, 0.1, 0.5, -1, FAKE, 64, None) == E                         # k_min < 0
+    assert mm(gp, FAKE, FAKE, 0.0, 0.5, 1, FAKE, 64, None) == E                          # scale
+    assert mm(gp, FAKE, FAKE, 0.1, 0.5, 1, FAKE, 8, None) == E                           # pitch < nb
+    assert mm(gp, None, FAKE, 0.1, 0.5, 1, FAKE, 64, None) == E
+    assert mm(gp, FAKE + 4, FAKE, 0.1, 0.5, 1, FAKE, 64, None) == E                      # misaligned
+    big = _geom(b=64, N=64 * 4097, Lq=1)
+    assert mm(ctypes.byref(big), FAKE, FAKE, 0.1, 0.5, 1, FAKE, 4160, None) == U          # nb > 4096
