@@ -46,10 +46,19 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_sources_digest() -> str:
+# The source file of each profiled kernel; its digest (with the shared internal header) tells whether a
+# stored counter measurement still describes the kernel being run.
+KERNEL_SOURCES = {"bsa_fwd": "attention.hip", "pack": "pack.hip", "permute": "permute.hip", "pool": "materialize.hip",
+                  "select": "materialize.hip", "union": "union_compact.hip", "counts": "accounting.hip",
+                  "merge": "merge.hip"}
+
+
+def kernel_sources_digest(kernel: str | None = None) -> str:
+    """Digest of one kernel's source file and the shared internal header (all sources when kernel is None)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_sparse_attention_rank_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    names = sorted(os.listdir(csrc)) if kernel is None else ["sparsp_internal.h", KERNEL_SOURCES[kernel]]
+    for name in names:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -62,7 +71,7 @@ def measured_traffic(kernel: str, workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("sources_digest") != kernel_sources_digest():
+    if rec.get("sources_digest") != kernel_sources_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -354,6 +363,19 @@ def main():
         print(f"[bench] {w.name}: communication accounting took {time.perf_counter() - t0:.1f} s", file=sys.stderr,
               flush=True)
 
+    # A plain device-to-device copy of the pack's byte count, as the achievable read + write rate.
+    cp_src = torch.empty(pack_bytes // 2, dtype=torch.uint8, device="cuda")
+    cp_dst = torch.empty_like(cp_src)
+    cp_dst.copy_(cp_src)
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    cev[0].record(stream)
+    for _ in range(5):
+        cp_dst.copy_(cp_src)
+    cev[1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * cp_src.numel() / (cev[0].elapsed_time(cev[1]) * 1e-3) / 1e9
+    del cp_src, cp_dst
+
     attn_tflops = attn_flops / (t_attn * 1e-3) / 1e12
     pack_gbs = pack_bytes / (t_pack * 1e-3) / 1e9
     rec = {
@@ -382,6 +404,8 @@ def main():
             "pack_us": round(t_pack * 1e3, 2),
             "pack_GBps": round(pack_gbs, 1),
             "pack_frac_hbm": round(pack_gbs / HBM_PEAK_GBS, 4),
+            "copy_ceiling_GBps": round(copy_gbs, 1),
+            "pack_frac_copy_ceiling": round(pack_gbs / copy_gbs, 4),
             "attn_ms": round(t_attn, 4),
             "attn_TFLOPs": round(attn_tflops, 2),
             "attn_frac_bf16": round(attn_tflops / BF16_DENSE_TFLOPS, 4),
@@ -415,7 +439,7 @@ def main():
         },
         "comm_volume": comm,
         "mask_materialisation": mat,
-        "sources_digest": kernel_sources_digest(),
+        "sources_digest": {k: kernel_sources_digest(k) for k in ("bsa_fwd", "pack")},
     }
     if not args.no_cpu:
         t0 = time.perf_counter()
