@@ -363,19 +363,6 @@ def main():
         print(f"[bench] {w.name}: communication accounting took {time.perf_counter() - t0:.1f} s", file=sys.stderr,
               flush=True)
 
-    # A plain device-to-device copy of the pack's byte count, as the achievable read + write rate.
-    cp_src = torch.empty(pack_bytes // 2, dtype=torch.uint8, device="cuda")
-    cp_dst = torch.empty_like(cp_src)
-    cp_dst.copy_(cp_src)
-    cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    cev[0].record(stream)
-    for _ in range(5):
-        cp_dst.copy_(cp_src)
-    cev[1].record(stream)
-    torch.cuda.synchronize()
-    copy_gbs = 5 * 2 * cp_src.numel() / (cev[0].elapsed_time(cev[1]) * 1e-3) / 1e9
-    del cp_src, cp_dst
-
     attn_tflops = attn_flops / (t_attn * 1e-3) / 1e12
     pack_gbs = pack_bytes / (t_pack * 1e-3) / 1e9
     rec = {
@@ -404,8 +391,6 @@ def main():
             "pack_us": round(t_pack * 1e3, 2),
             "pack_GBps": round(pack_gbs, 1),
             "pack_frac_hbm": round(pack_gbs / HBM_PEAK_GBS, 4),
-            "copy_ceiling_GBps": round(copy_gbs, 1),
-            "pack_frac_copy_ceiling": round(pack_gbs / copy_gbs, 4),
             "attn_ms": round(t_attn, 4),
             "attn_TFLOPs": round(attn_tflops, 2),
             "attn_frac_bf16": round(attn_tflops / BF16_DENSE_TFLOPS, 4),
