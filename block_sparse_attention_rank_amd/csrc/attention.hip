@@ -17,7 +17,12 @@
 // Pipeline.  Every selected key block is consumed in stages of 64 keys.  A stage (64 K rows and the
 // matching 64 columns of V^T, 2 x 64 x d bf16) is copied from global memory straight into LDS with
 // global_load_lds_dwordx4 (no register staging); the next stage's copy is issued before the current one
-// is computed, into the other of two LDS buffers, and two workgroups share a CU.  LDS rows are
+// is computed, into the other of two LDS buffers, and two workgroups share a CU.  The work is cut into
+// units of 32 keys.  At d = 128 a unit issues the next unit's score MFMAs beside its own softmax and then
+// its P V product, with two barriers per stage.  At d = 64, where the softmax costs twice as much per MFMA
+// flop, each unit's P V product is delayed to the next unit so that both products' MFMAs sit beside the
+// softmax arithmetic in one stretch of code, with one barrier per stage (measured: 5-11 % faster at d = 64,
+// 5 % slower at d = 128, where it needs all 256 VGPRs).  LDS rows are
 // XOR-swizzled in 16-byte chunks (chunk c of row m sits at c ^ swizzle(m)).  A 16-byte fragment read
 // is served 16 lanes at a time by 64 four-byte banks (256 bytes per clock), and its lanes read one
 // logical chunk of 16 consecutive rows, so the key gives those rows distinct bank groups; it also keeps
@@ -205,31 +210,38 @@ __device__ __forceinline__ void unit_accumulate(const unsigned char* vbuf, int g
       oacc[i] = mfma32(*reinterpret_cast<const bf16x8*>(vbuf + vread[2 * g + b] + i * 32 * T::VROW), pf[b], oacc[i]);
 }
 
-// Probabilities of a unit relative to the running maximum, without a per-unit maximum: they may reach
-// 2^64 (exact in fp32 and bf16, and the fp32 sums stay far from overflow).  The lane's 16-key sum, which
-// the row sum needs anyway, tells whether any probability went past 2^64 (or is inf or NaN: the first
-// unit of a row, whose maximum is still -inf); only then is the maximum taken, the state rescaled and
-// the probabilities recomputed.
+// The rare path of a unit's softmax.  Probabilities are first taken against the running maximum without a
+// per-unit maximum: they may reach 2^64 (exact in fp32 and bf16, and the fp32 sums stay far from overflow).
+// The lane's 16-key sum, which the row sum needs anyway, tells whether any probability went past 2^64 (or is
+// inf or NaN: the first unit of a row, whose maximum is still -inf); only then is this called: it takes the
+// unit's maximum, rescales the state (the accumulator already holds every earlier unit, including the one
+// whose P V product was issued in this unit, all relative to the old maximum) and recomputes the unit's
+// probabilities.
+template <int D, int B>
+__device__ __forceinline__ void unit_rescale(const f32x16& sacc, RowState<D, B>& rs, float scale_log2,
+                                                       bf16x8 (&pf)[2], float& lu) {
+  using T = Tile<D, B>;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[x]);
+  const float m_new = fmaxf(rs.m_run, max_halves(mx * scale_log2));  // scale_log2 > 0
+  if (m_new != -INFINITY) {  // -inf: no key of the row seen yet; nothing to rescale
+    const float alpha = rs.m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rs.m_run - m_new);
+    rs.m_run = m_new;
+    rs.l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < T::NDT; ++i) rs.oacc[i] *= alpha;
+  }
+  lu = 0.f;
+  unit_probabilities(sacc, scale_log2, m_new == -INFINITY ? 0.f : m_new, pf, lu);
+}
+
+// Softmax of a unit whose P V product follows at once (the d = 128 schedule).
 template <int D, int B>
 __device__ __forceinline__ void unit_softmax(const f32x16& sacc, RowState<D, B>& rs, float scale_log2, bf16x8 (&pf)[2]) {
-  using T = Tile<D, B>;
   float lu = 0.f;
   unit_probabilities(sacc, scale_log2, rs.m_run, pf, lu);
-  if (__builtin_amdgcn_ballot_w64(!(lu < 0x1p64f)) != 0) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) mx = fmaxf(mx, sacc[x]);
-    const float m_new = fmaxf(rs.m_run, max_halves(mx * scale_log2));  // scale_log2 > 0
-    if (m_new != -INFINITY) {  // -inf: no key of the row seen yet; nothing to rescale
-      const float alpha = rs.m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rs.m_run - m_new);
-      rs.m_run = m_new;
-      rs.l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < T::NDT; ++i) rs.oacc[i] *= alpha;
-    }
-    lu = 0.f;
-    unit_probabilities(sacc, scale_log2, m_new == -INFINITY ? 0.f : m_new, pf, lu);
-  }
+  if (__builtin_amdgcn_ballot_w64(!(lu < 0x1p64f)) != 0) unit_rescale<D, B>(sacc, rs, scale_log2, pf, lu);
   rs.l_run += lu;
 }
 
@@ -240,8 +252,9 @@ __device__ __forceinline__ void unit_softmax(const f32x16& sacc, RowState<D, B>&
 // (the compiler does not model the LDS write of a direct copy).
 template <int NOut>
 __device__ __forceinline__ void block_sync() {
-  static_assert(NOut >= 0 && NOut < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0070 | NOut);  // vmcnt(NOut) lgkmcnt(0), visible to the compiler's scoreboard
+  static_assert(NOut >= 0 && NOut < 64, "vmcnt field");
+  // s_waitcnt immediate: vmcnt bits 3:0 and 15:14, expcnt 6:4 (7: no wait), lgkmcnt 11:8 (0).
+  __builtin_amdgcn_s_waitcnt((NOut & 15) | ((NOut >> 4) << 14) | 0x0070);
   asm volatile("s_barrier" ::: "memory");
 }
 
@@ -290,6 +303,13 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   rs.m_run = -INFINITY;
   rs.l_run = 0.f;
 
+  // d = 64 schedule: the V^T buffers start at zero so that the first unit's empty pending product (0 x
+  // finite) adds nothing.
+  if constexpr (D == 64)
+    for (int i = t * 16; i < 2 * D * T::VROW; i += T::NT * 16)
+      *reinterpret_cast<uint4*>((i < D * T::VROW ? sV0 : sV1) + (i % (D * T::VROW))) = make_uint4(0u, 0u, 0u, 0u);
+  bf16x8 pfp[2];  // d = 64 schedule: probabilities of the unit whose P V product is still pending
+
   const uint8_t* mrow = mask + ((int64_t)h * Lq + k) * pitch;
   const int32_t* sof = slot_of + (int64_t)h * nb;
   const int tail_valid = N - (nb - 1) * B;  // real keys in the last block, 1..B
@@ -332,50 +352,116 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         return (code & 1) ? tail_valid - (s % T::NST) * kStageKeys - 32 * g - 8 * half : 32;
       };
 
-      // One unit: head of its scores, then the next unit's scores beside its probabilities, then its
-      // accumulation.  After the last unit the "next" scores read a stale buffer and are dropped.
-      auto unit = [&](f32x16& cur, f32x16& nxt, const unsigned char* kbuf_next, int g_next,
-                      const unsigned char* vbuf, int g, int lim) {
-        bf16x8 pf[2];
-        unit_mask(cur, lim);
-        nxt = unit_scores<D, B>(kbuf_next, g_next, kread, qf);
-        unit_softmax<D, B>(cur, rs, scale_log2, pf);
-        unit_accumulate<D, B>(vbuf, g, vread, pf, rs.oacc);
-      };
+      if constexpr (D == 64) {
+        // One unit u: the scores of unit u + 1, the probabilities of unit u and the P V product of unit u - 1
+        // (whose probabilities are already in pfp) are issued together, so the MFMAs of both products sit
+        // beside the softmax arithmetic in one stretch of code; the rare rescale follows.  After the last unit
+        // the "next" scores read a stale buffer and are dropped.
+        auto unit = [&](f32x16& cur, f32x16& nxt, const unsigned char* kbuf_next, int g_next,
+                        const unsigned char* vbuf_prev, int g_prev, int lim) {
+          bf16x8 pf[2];
+          float lu = 0.f;
+          unit_mask(cur, lim);
+          nxt = unit_scores<D, B>(kbuf_next, g_next, kread, qf);
+          unit_probabilities(cur, scale_log2, rs.m_run, pf, lu);
+          unit_accumulate<D, B>(vbuf_prev, g_prev, vread, pfp, rs.oacc);
+          if (__builtin_amdgcn_ballot_w64(!(lu < 0x1p64f)) != 0) unit_rescale<D, B>(cur, rs, scale_log2, pf, lu);
+          rs.l_run += lu;
+          pfp[0] = pf[0];
+          pfp[1] = pf[1];
+        };
 
-      // Copies: V^T[s + 1] is issued at the top of unit 2s (its buffer held V^T[s - 1], last read in unit
-      // 2s - 1), K[s + 2] at the top of unit 2s + 1 (its buffer held K[s], last read in unit 2s).  Each
-      // top waits for this lane's older copy and then for the whole workgroup, which makes V^T[s] (top of
-      // unit 2s) or K[s + 1] (top of unit 2s + 1) visible and frees the buffer it refills; the newer copy
-      // (CPT instructions) stays in flight when it was issued.
-      int c0 = code_of(0), c1 = code_of(1), c2 = code_of(2);  // codes of stages s, s + 1, s + 2
-      plan.issue_k(slot_ptr(c0), 0, sK0, wave);
-      plan.issue_v(slot_ptr(c0), 0, sV0, wave);
-      block_sync<0>();
-      if (n > 1) plan.issue_k(slot_ptr(c1), 1 % T::NST, sK1, wave);
-      f32x16 sa = unit_scores<D, B>(sK0, 0, kread, qf), sb;
+        // Copies, one barrier per 64-key stage: at the top of unit 2s + 1 every lane waits for all its copies
+        // (K[s + 1] and V^T[s], issued one stage earlier) and the workgroup meets, which makes them visible and
+        // frees K[s]'s buffer (last read by the scores of unit 2s + 1, issued in unit 2s) and V^T[s - 1]'s
+        // (last read by the P V product of unit 2s - 1, issued in unit 2s); K[s + 2] and V^T[s + 1] are then
+        // issued into them.  The first unit of a pass carries no pending product (pfp = 0 against a V^T
+        // buffer holding finite values).
+        int c0 = code_of(0), c1 = code_of(1), c2 = code_of(2);  // codes of stages s, s + 1, s + 2
+        pfp[0] = bf16x8{};
+        pfp[1] = bf16x8{};
+        // The Q fragment loads finished long ago; saying so here keeps the compiler from waiting on them
+        // (and with them on the copies issued after them) before the first scores.
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+        plan.issue_k(slot_ptr(c0), 0, sK0, wave);
+        plan.issue_k(slot_ptr(c1), 1 % T::NST, sK1, wave);
+        plan.issue_v(slot_ptr(c0), 0, sV0, wave);
+        block_sync<2 * T::CPT>();  // K[0] has landed (copies complete in issue order)
+        f32x16 sa = unit_scores<D, B>(sK0, 0, kread, qf), sb;
 
-      for (int s = 0; s < n; s += 2) {
-        // stage s (even): K[s] in sK0, V^T[s] in sV0, K[s + 1] in sK1
-        if (s + 1 < n) block_sync<T::CPT>(); else block_sync<0>();
-        if (s + 1 < n) plan.issue_v(slot_ptr(c1), (s + 1) % T::NST, sV1, wave);
-        int c3 = code_of(s + 3);
-        unit(sa, sb, sK0, 1, sV0, 0, lim_of(c0, s, 0));
-        if (s + 1 < n) block_sync<T::CPT>(); else block_sync<0>();
-        if (s + 2 < n) plan.issue_k(slot_ptr(c2), (s + 2) % T::NST, sK0, wave);
-        unit(sb, sa, sK1, 0, sV0, 1, lim_of(c0, s, 1));
-        if (s + 1 >= n) break;
-        c0 = c1; c1 = c2; c2 = c3;
+        for (int s = 0; s < n; s += 2) {
+          // stage s (even): K[s] in sK0, K[s + 1] in sK1 and V^T[s] in sV0 landing, V^T[s - 1] in sV1
+          int c3 = code_of(s + 3);
+          unit(sa, sb, sK0, 1, sV1, 1, lim_of(c0, s, 0));
+          block_sync<0>();
+          if (s + 2 < n) plan.issue_k(slot_ptr(c2), (s + 2) % T::NST, sK0, wave);
+          if (s + 1 < n) plan.issue_v(slot_ptr(c1), (s + 1) % T::NST, sV1, wave);
+          unit(sb, sa, sK1, 0, sV0, 0, lim_of(c0, s, 1));
+          if (s + 1 >= n) {
+            unit_accumulate<D, B>(sV0, 1, vread, pfp, rs.oacc);
+            break;
+          }
+          c0 = c1; c1 = c2; c2 = c3;
 
-        // stage s + 1 (odd): K[s + 1] in sK1, V^T[s + 1] in sV1, K[s + 2] in sK0
-        if (s + 2 < n) block_sync<T::CPT>(); else block_sync<0>();
-        if (s + 2 < n) plan.issue_v(slot_ptr(c1), (s + 2) % T::NST, sV0, wave);
-        c3 = code_of(s + 4);
-        unit(sa, sb, sK1, 1, sV1, 0, lim_of(c0, s + 1, 0));
-        if (s + 2 < n) block_sync<T::CPT>(); else block_sync<0>();
-        if (s + 3 < n) plan.issue_k(slot_ptr(c2), (s + 3) % T::NST, sK1, wave);
-        unit(sb, sa, sK0, 0, sV1, 1, lim_of(c0, s + 1, 1));
-        c0 = c1; c1 = c2; c2 = c3;
+          // stage s + 1 (odd): K[s + 1] in sK1, K[s + 2] in sK0 and V^T[s + 1] in sV1 landing, V^T[s] in sV0
+          c3 = code_of(s + 4);
+          unit(sa, sb, sK1, 1, sV0, 1, lim_of(c0, s + 1, 0));
+          block_sync<0>();
+          if (s + 3 < n) plan.issue_k(slot_ptr(c2), (s + 3) % T::NST, sK1, wave);
+          if (s + 2 < n) plan.issue_v(slot_ptr(c1), (s + 2) % T::NST, sV0, wave);
+          unit(sb, sa, sK0, 0, sV1, 0, lim_of(c0, s + 1, 1));
+          if (s + 2 >= n) {
+            unit_accumulate<D, B>(sV1, 1, vread, pfp, rs.oacc);
+            break;
+          }
+          c0 = c1; c1 = c2; c2 = c3;
+        }
+      } else {
+        // One unit: head of its scores, then the next unit's scores beside its probabilities, then its
+        // accumulation.  After the last unit the "next" scores read a stale buffer and are dropped.
+        auto unit = [&](f32x16& cur, f32x16& nxt, const unsigned char* kbuf_next, int g_next,
+                        const unsigned char* vbuf, int g, int lim) {
+          bf16x8 pf[2];
+          unit_mask(cur, lim);
+          nxt = unit_scores<D, B>(kbuf_next, g_next, kread, qf);
+          unit_softmax<D, B>(cur, rs, scale_log2, pf);
+          unit_accumulate<D, B>(vbuf, g, vread, pf, rs.oacc);
+        };
+
+        // Copies: V^T[s + 1] is issued at the top of unit 2s (its buffer held V^T[s - 1], last read in unit
+        // 2s - 1), K[s + 2] at the top of unit 2s + 1 (its buffer held K[s], last read in unit 2s).  Each
+        // top waits for this lane's older copy and then for the whole workgroup, which makes V^T[s] (top of
+        // unit 2s) or K[s + 1] (top of unit 2s + 1) visible and frees the buffer it refills; the newer copy
+        // (CPT instructions) stays in flight when it was issued.
+        int c0 = code_of(0), c1 = code_of(1), c2 = code_of(2);  // codes of stages s, s + 1, s + 2
+        plan.issue_k(slot_ptr(c0), 0, sK0, wave);
+        plan.issue_v(slot_ptr(c0), 0, sV0, wave);
+        block_sync<0>();
+        if (n > 1) plan.issue_k(slot_ptr(c1), 1 % T::NST, sK1, wave);
+        f32x16 sa = unit_scores<D, B>(sK0, 0, kread, qf), sb;
+
+        for (int s = 0; s < n; s += 2) {
+          // stage s (even): K[s] in sK0, V^T[s] in sV0, K[s + 1] in sK1
+          if (s + 1 < n) block_sync<T::CPT>(); else block_sync<0>();
+          if (s + 1 < n) plan.issue_v(slot_ptr(c1), (s + 1) % T::NST, sV1, wave);
+          int c3 = code_of(s + 3);
+          unit(sa, sb, sK0, 1, sV0, 0, lim_of(c0, s, 0));
+          if (s + 1 < n) block_sync<T::CPT>(); else block_sync<0>();
+          if (s + 2 < n) plan.issue_k(slot_ptr(c2), (s + 2) % T::NST, sK0, wave);
+          unit(sb, sa, sK1, 0, sV0, 1, lim_of(c0, s, 1));
+          if (s + 1 >= n) break;
+          c0 = c1; c1 = c2; c2 = c3;
+
+          // stage s + 1 (odd): K[s + 1] in sK1, V^T[s + 1] in sV1, K[s + 2] in sK0
+          if (s + 2 < n) block_sync<T::CPT>(); else block_sync<0>();
+          if (s + 2 < n) plan.issue_v(slot_ptr(c1), (s + 2) % T::NST, sV0, wave);
+          c3 = code_of(s + 4);
+          unit(sa, sb, sK1, 1, sV1, 0, lim_of(c0, s + 1, 0));
+          if (s + 2 < n) block_sync<T::CPT>(); else block_sync<0>();
+          if (s + 3 < n) plan.issue_k(slot_ptr(c2), (s + 3) % T::NST, sK1, wave);
+          unit(sb, sa, sK0, 0, sV1, 1, lim_of(c0, s + 1, 1));
+          c0 = c1; c1 = c2; c2 = c3;
+        }
       }
     }
     __syncthreads();  // sList and the buffers are reused by the next pass
