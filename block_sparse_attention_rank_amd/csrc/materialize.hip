@@ -20,7 +20,6 @@ namespace sparsp {
 namespace {
 
 constexpr int kPoolThreads = 256;
-constexpr int kSelectThreads = 256;
 
 template <int D, int B>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const uint16_t* __restrict__ X, int n_blocks,
@@ -69,16 +68,18 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-template <int D>
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(const float* __restrict__ qp, const float* __restrict__ kp,
+// NT threads: 256 for rows of up to 1024 blocks, 1024 above (the sort's passes are separated by barriers,
+// so more threads per row shorten every pass).
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qp, const float* __restrict__ kp,
                                                                 int Lq, int nb, int np2, float scale, float tau,
                                                                 int k_min, uint8_t* __restrict__ mask, int64_t pitch) {
   extern __shared__ __align__(16) unsigned char smem[];
   uint64_t* keys = reinterpret_cast<uint64_t*>(smem);        // [np2]
   float* cum = reinterpret_cast<float*>(keys + np2);          // [np2]
   float* qv = cum + np2;                                      // [D]
-  int* wsum = reinterpret_cast<int*>(qv + D);                 // scan scratch: [kSelectThreads / 64] floats
-  uint8_t* sel = reinterpret_cast<uint8_t*>(wsum + 8);        // [pitch]
+  int* wsum = reinterpret_cast<int*>(qv + D);                 // scan scratch: one entry per wave (<= 16)
+  uint8_t* sel = reinterpret_cast<uint8_t*>(wsum + 16);       // [pitch]
 
   const int k = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   if (t < D) qv[t] = qp[((int64_t)h * Lq + k) * D + t];
@@ -86,7 +87,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const float* __r
 
   // Scores, keyed so that an ascending sort gives descending score and, among equal scores, ascending j.
   const float4* kh = reinterpret_cast<const float4*>(kp + (int64_t)h * nb * D);
-  for (int j = t; j < np2; j += kSelectThreads) {
+  for (int j = t; j < np2; j += NT) {
     uint64_t key = ~0ull;
     if (j < nb) {
       float s = 0.f;
@@ -99,13 +100,13 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const float* __r
     }
     keys[j] = key;
   }
-  for (int i = t; i < pitch; i += kSelectThreads) sel[i] = 0;
+  for (int i = t; i < pitch; i += NT) sel[i] = 0;
   __syncthreads();
 
   // Bitonic sort, ascending, of np2 keys (np2 a power of two).
   for (int size = 2; size <= np2; size <<= 1)
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = t; i < np2; i += kSelectThreads) {
+      for (int i = t; i < np2; i += NT) {
         const int p = i ^ stride;
         if (p > i) {
           const uint64_t a = keys[i], b = keys[p];
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const float* __r
   // Softmax weights in sorted order and their inclusive prefix sums.  Each thread scans a run of
   // consecutive entries; the runs' totals are scanned across the workgroup in thread order.
   const float smax = from_ordered_bits(~(uint32_t)(keys[0] >> 32));
-  const int per = (np2 + kSelectThreads - 1) / kSelectThreads;
+  const int per = (np2 + NT - 1) / NT;
   const int i0 = t * per;
   float run = 0.f;
   for (int i = i0; i < min(i0 + per, nb); ++i) {
@@ -148,20 +149,20 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(const float* __r
   // n_tau = 1 + the number of prefixes still short of tau of the total mass (cum is nondecreasing).
   const float target = tau * cum[nb - 1];
   int below = 0;
-  for (int i = t; i < nb; i += kSelectThreads) below += cum[i] < target ? 1 : 0;
+  for (int i = t; i < nb; i += NT) below += cum[i] < target ? 1 : 0;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) below += __shfl_xor(below, off, 64);
   __syncthreads();
   if (lane == 0) wsum[wave] = below;
   __syncthreads();
   int n_tau = 1;
-  for (int w = 0; w < kSelectThreads / 64; ++w) n_tau += wsum[w];
+  for (int w = 0; w < NT / 64; ++w) n_tau += wsum[w];
   const int n = min(nb, max(k_min, n_tau));
 
-  for (int i = t; i < n; i += kSelectThreads) sel[(uint32_t)keys[i]] = 1;
+  for (int i = t; i < n; i += NT) sel[(uint32_t)keys[i]] = 1;
   __syncthreads();
   uint8_t* row = mask + ((int64_t)h * Lq + k) * pitch;
-  for (int i = t * 16; i < pitch; i += kSelectThreads * 16)
+  for (int i = t * 16; i < pitch; i += NT * 16)
     *reinterpret_cast<uint4*>(row + i) = *reinterpret_cast<const uint4*>(sel + i);
 }
 
@@ -182,7 +183,7 @@ hipError_t launch_pool_d(const Dims& g, const uint16_t* X, int n_blocks, const i
 size_t select_lds_bytes(int nb, int d, int64_t pitch) {
   int np2 = 4;
   while (np2 < nb) np2 <<= 1;
-  return (size_t)np2 * 12 + (size_t)d * 4 + 32 + (size_t)pitch;
+  return (size_t)np2 * 12 + (size_t)d * 4 + 64 + (size_t)pitch;
 }
 
 hipError_t launch_pool(const Dims& g, const uint16_t* X, int n_blocks, const int32_t* block_ids, float* pooled,
@@ -199,11 +200,18 @@ hipError_t launch_select(const Dims& g, const float* q_pooled, const float* k_po
   while (np2 < g.nb) np2 <<= 1;
   const size_t lds = select_lds_bytes(g.nb, g.d, pitch);
   const dim3 grid((unsigned)g.Lq, (unsigned)g.H);
-  if (g.d == 128)
-    hipLaunchKernelGGL(select_kernel<128>, grid, dim3(kSelectThreads), lds, stream, q_pooled, k_pooled, g.Lq, g.nb, np2,
+  const bool wide = np2 > 1024;
+  if (g.d == 128 && wide)
+    hipLaunchKernelGGL((select_kernel<128, 1024>), grid, dim3(1024), lds, stream, q_pooled, k_pooled, g.Lq, g.nb,
+                       np2, scale, tau, k_min, mask, pitch);
+  else if (g.d == 128)
+    hipLaunchKernelGGL((select_kernel<128, 256>), grid, dim3(256), lds, stream, q_pooled, k_pooled, g.Lq, g.nb, np2,
                        scale, tau, k_min, mask, pitch);
+  else if (wide)
+    hipLaunchKernelGGL((select_kernel<64, 1024>), grid, dim3(1024), lds, stream, q_pooled, k_pooled, g.Lq, g.nb,
+                       np2, scale, tau, k_min, mask, pitch);
   else
-    hipLaunchKernelGGL(select_kernel<64>, grid, dim3(kSelectThreads), lds, stream, q_pooled, k_pooled, g.Lq, g.nb, np2,
+    hipLaunchKernelGGL((select_kernel<64, 256>), grid, dim3(256), lds, stream, q_pooled, k_pooled, g.Lq, g.nb, np2,
                        scale, tau, k_min, mask, pitch);
   return hipGetLastError();
 }

@@ -109,6 +109,9 @@ CASES = {
     "d64_b128_ragged": (custom(H=2, d=64, T=3, HW=1000, b=128, G=3), 0.95, 1),
     "floor_everything": (custom(H=2, d=64, T=2, HW=700, b=64, G=2), 0.1, 10_000),
     "tau_one": (custom(H=2, d=128, T=2, HW=700, b=64, G=2), 1.0, 0),
+    # rows of more than 1024 blocks take the 1024-thread select
+    "wide_d64": (custom(H=2, d=64, T=12, HW=6144, b=64, G=8, k_offset_sigma=3.0), 0.9, 16),
+    "wide_d128_ragged": (custom(H=1, d=128, T=37, HW=3600, b=128, G=8), 0.5, 4),
 }
 
 
