@@ -425,7 +425,11 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
           unit_mask(cur, lim);
           nxt = unit_scores<D, B>(kbuf_next, g_next, kread, qf);
           unit_softmax<D, B>(cur, rs, scale_log2, pf);
+          // The P V cluster runs at raised wave priority: the SIMD's other wave is mid-softmax, and
+          // letting this wave's MFMAs issue first keeps the matrix pipe fed (measured 3 % faster).
+          __builtin_amdgcn_s_setprio(1);
           unit_accumulate<D, B>(vbuf, g, vread, pf, rs.oacc);
+          __builtin_amdgcn_s_setprio(0);
         };
 
         // Copies: V^T[s + 1] is issued at the top of unit 2s (its buffer held V^T[s - 1], last read in unit
