@@ -301,6 +301,29 @@ def main():
     print(f"[bench] {w.name}: segmented attention {seg_total:.3f} ms ({len(order)} segments), merge "
           f"{merge_ms * 1e3:.1f} us each", file=sys.stderr, flush=True)
 
+    # The same consumption with the fused call: each segment folded straight into the running result.
+    def fused_step():
+        accO.zero_()
+        accL.fill_(float("-inf"))
+        for p in order:
+            bsa.block_sparse_attn_segment_accumulate(g, Q, mask, u.slot_of, packed, ranges[p][0], ranges[p][1], accO,
+                                                     accL, scale)
+
+    fused_step()
+    torch.cuda.synchronize()
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(seg_steps)]
+    for e in fev:
+        accO.zero_()
+        accL.fill_(float("-inf"))
+        e[0].record(stream)
+        for p in order:
+            bsa.block_sparse_attn_segment_accumulate(g, Q, mask, u.slot_of, packed, ranges[p][0], ranges[p][1], accO,
+                                                     accL, scale)
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    fused_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in fev]))
+    print(f"[bench] {w.name}: segmented attention, fused fold {fused_ms:.3f} ms", file=sys.stderr, flush=True)
+
     # Placement permutation (section 4.3) of the layer's hidden states [nb*b][H*d] bf16 into rank-major
     # block order and back: each call reads and writes every byte once.
     pos, _ = bsa.placement_permutation(inp["placement"], g.G)
@@ -397,6 +420,8 @@ def main():
             "segmented_attn_ms": round(seg_total, 4),
             "segmented_attn_TFLOPs": round(attn_flops / (seg_total * 1e-3) / 1e12, 2),
             "merge_us": round(merge_ms * 1e3, 2),
+            "segmented_fused_attn_ms": round(fused_ms, 4),
+            "segmented_fused_attn_TFLOPs": round(attn_flops / (fused_ms * 1e-3) / 1e12, 2),
             "merge_GBps": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1) if merge_ms > 0 else None,
             "permute_hidden_bytes": perm_bytes,
             "permute_us": round(t_perm * 1e3, 2),

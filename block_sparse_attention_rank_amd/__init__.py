@@ -17,7 +17,8 @@ import numpy as np
 from ._lib import EXPORTS, LIB_PATH, Geometry, SparspError, check, load  # noqa: F401
 
 __all__ = ["Geometry", "SparspError", "UnionResult", "geometry", "local_query_blocks", "demand_union",
-           "pack_kv", "block_sparse_attn", "block_sparse_attn_segment", "merge_partial", "segment_ranges",
+           "pack_kv", "block_sparse_attn", "block_sparse_attn_segment", "block_sparse_attn_segment_accumulate",
+           "merge_partial", "segment_ranges",
            "placement_permutation", "permute_blocks", "demand_counts", "comm_volume", "pool_blocks",
            "materialize_mask", "load", "LIB_PATH", "EXPORTS"]
 
@@ -161,6 +162,26 @@ def block_sparse_attn_segment(g: Geometry, Q, mask, slot_of, packed, slot_lo: in
     check(load().sparsp_block_sparse_attn_segment(ctypes.byref(g), _ptr(Q), _ptr(mask), mask.shape[2],
                                                   _ptr(slot_of), _ptr(packed), int(slot_lo), int(slot_hi), scale,
                                                   _ptr(O), _ptr(lse), _stream(stream)))
+    return O, lse
+
+
+def block_sparse_attn_segment_accumulate(g: Geometry, Q, mask, slot_of, packed, slot_lo: int, slot_hi: int, O, lse,
+                                         softmax_scale: float | None = None, stream=None):
+    """Fold the attention over the selected blocks whose slot lies in [slot_lo, slot_hi) into the running
+    (O, lse) in place (sparsp_block_sparse_attn_segment_accumulate); start from (0, -inf)."""
+    import torch
+    _require(Q, "Q", torch.bfloat16, (g.H, g.Lq * g.b, g.d))
+    _require(mask, "mask", torch.uint8)
+    _require(slot_of, "slot_of", torch.int32, (g.H, g.nb))
+    _require(packed, "packed", torch.bfloat16)
+    _require(O, "O", torch.float32, (g.H, g.Lq * g.b, g.d))
+    _require(lse, "lse", torch.float32, (g.H, g.Lq * g.b))
+    if slot_hi > packed.shape[0]:
+        raise ValueError("packed holds fewer than slot_hi slots")
+    scale = 1.0 / math.sqrt(g.d) if softmax_scale is None else float(softmax_scale)
+    check(load().sparsp_block_sparse_attn_segment_accumulate(ctypes.byref(g), _ptr(Q), _ptr(mask), mask.shape[2],
+                                                             _ptr(slot_of), _ptr(packed), int(slot_lo), int(slot_hi),
+                                                             scale, _ptr(O), _ptr(lse), _stream(stream)))
     return O, lse
 
 

@@ -27,6 +27,7 @@ EXPORTS = (
     "sparsp_block_sparse_attn",
     "sparsp_block_sparse_attn_segment",
     "sparsp_merge_partial",
+    "sparsp_block_sparse_attn_segment_accumulate",
     "sparsp_placement_permutation",
     "sparsp_permute_blocks",
     "sparsp_demand_counts",
@@ -86,6 +87,8 @@ def load() -> ctypes.CDLL:
     lib.sparsp_block_sparse_attn.argtypes = [gp, P, P, i64, P, P, i32, f32, P, P, P]
     lib.sparsp_block_sparse_attn_segment.restype = i32
     lib.sparsp_block_sparse_attn_segment.argtypes = [gp, P, P, i64, P, P, i32, i32, f32, P, P, P]
+    lib.sparsp_block_sparse_attn_segment_accumulate.restype = i32
+    lib.sparsp_block_sparse_attn_segment_accumulate.argtypes = [gp, P, P, i64, P, P, i32, i32, f32, P, P, P]
     lib.sparsp_merge_partial.restype = i32
     lib.sparsp_merge_partial.argtypes = [gp, P, P, P, P, P]
     lib.sparsp_placement_permutation.restype = i32

@@ -140,7 +140,7 @@ namespace {
 // Shared checks and launch of the attention entry points over the slot range [slot_lo, slot_hi).
 int32_t attention_call(const char* fn, const sparsp_geometry* geom, const uint16_t* Q, const uint8_t* mask,
                        int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed, int32_t slot_lo,
-                       int32_t slot_hi, float softmax_scale, float* O, float* lse, void* stream) {
+                       int32_t slot_hi, float softmax_scale, float* O, float* lse, void* stream, int accumulate = 0) {
   sparsp::Dims d;
   int32_t st = check_geometry(geom, fn, &d);
   if (st) return st;
@@ -151,7 +151,7 @@ int32_t attention_call(const char* fn, const sparsp_geometry* geom, const uint16
   if ((Q && !aligned16(Q)) || (packed && !aligned16(packed)) || (O && !aligned16(O)))
     return fail(SPARSP_ERR_INVALID, fn, "Q, packed and O must be 16-byte aligned");
   return hip_status(sparsp::launch_attention(d, Q, mask, mask_pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale,
-                                             O, lse, reinterpret_cast<hipStream_t>(stream)),
+                                             O, lse, accumulate, reinterpret_cast<hipStream_t>(stream)),
                     fn);
 }
 
@@ -174,6 +174,16 @@ int32_t sparsp_block_sparse_attn_segment(const sparsp_geometry* geom, const uint
   if (slot_lo < 0 || slot_hi < slot_lo) return fail(SPARSP_ERR_INVALID, fn, "need 0 <= slot_lo <= slot_hi");
   return attention_call(fn, geom, Q, mask, mask_pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse,
                         stream);
+}
+
+int32_t sparsp_block_sparse_attn_segment_accumulate(const sparsp_geometry* geom, const uint16_t* Q,
+                                                    const uint8_t* mask, int64_t mask_pitch, const int32_t* slot_of,
+                                                    const uint16_t* packed, int32_t slot_lo, int32_t slot_hi,
+                                                    float softmax_scale, float* O, float* lse, void* stream) {
+  static const char* fn = "sparsp_block_sparse_attn_segment_accumulate";
+  if (slot_lo < 0 || slot_hi < slot_lo) return fail(SPARSP_ERR_INVALID, fn, "need 0 <= slot_lo <= slot_hi");
+  return attention_call(fn, geom, Q, mask, mask_pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse,
+                        stream, 1);
 }
 
 int32_t sparsp_merge_partial(const sparsp_geometry* geom, float* O, float* lse, const float* O_part,

@@ -262,7 +262,7 @@ template <int D, int B>
 __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) void bsa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint8_t* __restrict__ mask, int64_t pitch,
     const int32_t* __restrict__ slot_of, const uint16_t* __restrict__ packed, int slot_lo, int slot_hi, float scale_log2,
-    int H, int Lq, int nb, int N, float* __restrict__ O, float* __restrict__ lse) {
+    int H, int Lq, int nb, int N, float* __restrict__ O, float* __restrict__ lse, int accumulate) {
   using T = Tile<D, B>;
   // Separate double buffers for K and V^T.  The work is cut into units of 32 keys (two per stage); the
   // scores of unit u + 1 are computed while unit u is turned into probabilities, and then unit u is
@@ -316,6 +316,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   const char* pk = reinterpret_cast<const char*>(packed);
 
   int col = 0;
+  int seen = 0;  // selected blocks in the slot range, over all passes
   while (col < nb) {
     // List the selected blocks of the next columns (ascending j) as (slot << 1 | is_last_block).
     int total = 0;
@@ -342,6 +343,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       __syncthreads();
     }
 
+    seen += total;
     const int n = total * T::NST;  // stages of this pass
     if (n > 0) {
       // Slot code of stage s (clamped to the last stage: codes past the end are only read, never used).
@@ -472,8 +474,33 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   }
 
   const float l_tot = sum_halves(rs.l_run);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse_part = l_tot > 0.f ? rs.m_run * 0.69314718055994531f + logf(l_tot) : -INFINITY;
   float* orow = O + row * D;
+  if (accumulate) {
+    // Fold this partial result into the running one held in O and lse (the online softmax of whole pieces
+    // of KV): lse <- ln(e^lse + e^lse_part), O <- e^(lse_old - lse) O + e^(lse_part - lse) O_part.  An
+    // item without any selected block in the range leaves its rows as they are.
+    if (seen == 0) return;
+    const float lse_old = lse[row];
+    const float m = fmaxf(lse_old, lse_part);
+    if (m == -INFINITY) return;  // both empty: the row stays (0, -inf) or as it was
+    const float w_old = expf(lse_old - m), w_part = expf(lse_part - m);
+    const float wsum = w_old + w_part;
+    const float a = w_old / wsum;
+    const float c = l_tot > 0.f ? (w_part / wsum) / l_tot : 0.f;
+#pragma unroll
+    for (int i = 0; i < T::NDT; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float4* dst = reinterpret_cast<float4*>(orow + i * 32 + q * 8 + half * 4);
+        const float4 o = *dst;
+        *dst = make_float4(a * o.x + c * rs.oacc[i][4 * q + 0], a * o.y + c * rs.oacc[i][4 * q + 1],
+                           a * o.z + c * rs.oacc[i][4 * q + 2], a * o.w + c * rs.oacc[i][4 * q + 3]);
+      }
+    if (half == 0) lse[row] = m + logf(wsum);
+    return;
+  }
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
   for (int i = 0; i < T::NDT; ++i)
 #pragma unroll
@@ -482,20 +509,20 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
                                    rs.oacc[i][4 * q + 2] * inv, rs.oacc[i][4 * q + 3] * inv);
       *reinterpret_cast<float4*>(orow + i * 32 + q * 8 + half * 4) = v;
     }
-  if (half == 0) lse[row] = l_tot > 0.f ? rs.m_run * 0.69314718055994531f + logf(l_tot) : -INFINITY;
+  if (half == 0) lse[row] = lse_part;
 }
 
 template <int D, int B>
 hipError_t launch_attention_t(const Dims& g, const uint16_t* Q, const uint8_t* mask, int64_t pitch,
                               const int32_t* slot_of, const uint16_t* packed, int32_t slot_lo, int32_t slot_hi,
-                              float softmax_scale, float* O, float* lse, hipStream_t stream) {
+                              float softmax_scale, float* O, float* lse, int accumulate, hipStream_t stream) {
   const int64_t items = (int64_t)g.H * g.Lq;
   if (items == 0) return hipSuccess;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
   constexpr int64_t round = (int64_t)kXcds * kXcdChunk;
   const int64_t grid = (items + round - 1) / round * round;
   hipLaunchKernelGGL((bsa_fwd_kernel<D, B>), dim3((unsigned)grid), dim3(2 * B), 0, stream, Q, mask, pitch,
-                     slot_of, packed, slot_lo, slot_hi, scale_log2, g.H, g.Lq, g.nb, g.N, O, lse);
+                     slot_of, packed, slot_lo, slot_hi, scale_log2, g.H, g.Lq, g.nb, g.N, O, lse, accumulate);
   return hipGetLastError();
 }
 
@@ -503,17 +530,17 @@ hipError_t launch_attention_t(const Dims& g, const uint16_t* Q, const uint8_t* m
 
 hipError_t launch_attention(const Dims& g, const uint16_t* Q, const uint8_t* mask, int64_t pitch,
                             const int32_t* slot_of, const uint16_t* packed, int32_t slot_lo, int32_t slot_hi,
-                            float softmax_scale, float* O, float* lse, hipStream_t stream) {
+                            float softmax_scale, float* O, float* lse, int accumulate, hipStream_t stream) {
   if (g.d == 128 && g.b == 128)
-    return launch_attention_t<128, 128>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse,
+    return launch_attention_t<128, 128>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse, accumulate,
                                         stream);
   if (g.d == 64 && g.b == 64)
-    return launch_attention_t<64, 64>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse,
+    return launch_attention_t<64, 64>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse, accumulate,
                                       stream);
   if (g.d == 128 && g.b == 64)
-    return launch_attention_t<128, 64>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse,
+    return launch_attention_t<128, 64>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse, accumulate,
                                        stream);
-  return launch_attention_t<64, 128>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse,
+  return launch_attention_t<64, 128>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse, accumulate,
                                      stream);
 }
 

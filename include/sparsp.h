@@ -19,11 +19,11 @@
  *   4. sparsp_block_sparse_attn   -- softmax(Q K^T / sqrt(d)) V (section 2.2) over the selected key
  *                                    blocks only, with an online softmax (section 2.3), reading K/V
  *                                    from the compacted buffer.
- *   5. sparsp_block_sparse_attn_segment, sparsp_merge_partial
+ *   5. sparsp_block_sparse_attn_segment, sparsp_merge_partial, sparsp_block_sparse_attn_segment_accumulate
  *                                 -- the same attention restricted to one range of packed slots (one
  *                                    source rank's segment, consumed as it arrives: sections 5.1 and
- *                                    7), and the log-sum-exp merge of such partial results (section
- *                                    2.3's online softmax across pieces of KV).
+ *                                    7), the log-sum-exp merge of such partial results (section 2.3's
+ *                                    online softmax across pieces of KV), and both fused in one call.
  *   6. sparsp_placement_permutation, sparsp_permute_blocks
  *                                 -- the placement realised as a permutation of whole blocks into
  *                                    rank-major order, applied to hidden states and undone afterwards
@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define SPARSP_ABI_VERSION 5
+#define SPARSP_ABI_VERSION 6
 
 typedef enum sparsp_status {
   SPARSP_OK = 0,
@@ -181,6 +181,24 @@ int32_t sparsp_block_sparse_attn_segment(const sparsp_geometry* g, const uint16_
                                          int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed,
                                          int32_t slot_lo, int32_t slot_hi, float softmax_scale, float* O,
                                          float* lse, void* stream);
+
+/*
+ * sparsp_block_sparse_attn_segment and sparsp_merge_partial in one call (sections 2.3, 5.1 and 7): the
+ * attention over the selected blocks whose slot lies in [slot_lo, slot_hi) is folded straight into the
+ * running result instead of being written out and merged.  DEVICE pointers; arguments as for
+ * sparsp_block_sparse_attn_segment, except
+ *   O, lse       [H][Lq*b][d], [H][Lq*b] float32: the running result over the keys consumed so far (read,
+ *                written); start from (0, -inf).  With lse_part and O_part the segment's result, lse <-
+ *                ln(e^lse + e^lse_part) and O <- e^(lse_old - lse) O + e^(lse_part - lse) O_part.  Rows
+ *                of a query block none of whose selected blocks lies in the range are not touched.
+ * Calling it for every segment of the payload, in any order, gives the result of sparsp_block_sparse_attn
+ * up to rounding.  Calls that update the same O and lse must be ordered (e.g. one stream).
+ * Errors: as for sparsp_block_sparse_attn_segment.
+ */
+int32_t sparsp_block_sparse_attn_segment_accumulate(const sparsp_geometry* g, const uint16_t* Q, const uint8_t* mask,
+                                                    int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed,
+                                                    int32_t slot_lo, int32_t slot_hi, float softmax_scale, float* O,
+                                                    float* lse, void* stream);
 
 /*
  * Fold a partial attention result over one key set into a running result over a disjoint key set (section

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = bsa.load()
-    assert lib.sparsp_abi_version() == 5
+    assert lib.sparsp_abi_version() == 6
     assert lib.sparsp_status_string(0) == b"ok"
     assert lib.sparsp_status_string(1) == b"invalid argument"
     assert lib.sparsp_status_string(2) == b"unsupported configuration"

@@ -250,3 +250,71 @@ def test_segments_and_merge(require_gpu, name):
     # bf16 (relative to each piece's running maximum), so they agree to the sum of the two distances
     assert d_single.max() <= 2 * MAX_ABS, d_single.max()
     print(f"[parity] segments {name}: merged max {mx:.2e}, vs single pass {d_single.max():.2e}", flush=True)
+
+
+@pytest.mark.parametrize("name", list(SEGMENT_CASES))
+def test_segment_accumulate(require_gpu, name):
+    """The fused segment call folds each segment into the running (O, lse) in place, in ring order and in
+    reverse order: the result matches the oracle's full attention and the two-call path (segment + merge)."""
+    import torch
+    import block_sparse_attention_rank_amd as bsa
+    from _gpu import run_path
+    w = SEGMENT_CASES[name]
+    inp = _inputs(name) if w is None else make_inputs(w)
+    w = inp["workload"]
+    print(f"[parity] segment accumulate {name}", flush=True)
+    res = run_path(inp)
+    g, u, dev = res["g"], res["union"], res["dev"]
+    ranges = bsa.segment_ranges(u.seg_offsets.cpu().numpy(), w.H, w.G)
+    Lq = len(inp["q_blocks"])
+    items = [(h, k) for h in range(w.H) for k in range(Lq)] if w.H * Lq <= 300 else _sample_items(inp, n_rand=3)
+    scale = 1.0 / math.sqrt(w.d)
+    ring = [(w.r + k) % w.G for k in range(w.G)]
+    results = []
+    for order in (ring, ring[::-1]):
+        O_run = torch.zeros_like(res["O"])
+        lse_run = torch.full_like(res["lse"], float("-inf"))
+        two_O = torch.zeros_like(res["O"])
+        two_lse = torch.full_like(res["lse"], float("-inf"))
+        for p in order:
+            lo, hi = ranges[p]
+            bsa.block_sparse_attn_segment_accumulate(g, dev["Q"], dev["mask"], u.slot_of, res["packed"], lo, hi,
+                                                     O_run, lse_run, scale)
+            O_p, lse_p = bsa.block_sparse_attn_segment(g, dev["Q"], dev["mask"], u.slot_of, res["packed"], lo, hi,
+                                                       scale)
+            bsa.merge_partial(g, two_O, two_lse, O_p, lse_p)
+        torch.cuda.synchronize()
+        _check_attention(inp, O_run.cpu().numpy(), lse_run.cpu().numpy(), items)
+        real = O.real_rows(inp["q_blocks"], w.b, w.N)
+        # the fused and two-call paths round the same partial results; only the merge arithmetic differs
+        d_two = np.abs(O_run.cpu().numpy()[:, real] - two_O.cpu().numpy()[:, real])
+        assert d_two.max() <= 1e-5, d_two.max()
+        l_run, l_two = lse_run.cpu().numpy()[:, real], two_lse.cpu().numpy()[:, real]
+        assert np.array_equal(np.isfinite(l_run), np.isfinite(l_two))
+        fin = np.isfinite(l_two)
+        assert np.abs(l_run[fin] - l_two[fin]).max() <= 1e-5 * max(1.0, float(np.abs(l_two[fin]).max()))
+        results.append(O_run.cpu().numpy()[:, real])
+    assert np.abs(results[0] - results[1]).max() <= 2 * MAX_ABS
+
+
+def test_segment_accumulate_leaves_untouched_rows(require_gpu):
+    """A segment with no selected block for some query blocks leaves their running rows bit-for-bit as they
+    were (here: a sentinel), and an empty slot range touches nothing."""
+    import torch
+    import block_sparse_attention_rank_amd as bsa
+    from _gpu import run_path
+    inp = make_inputs(custom(H=2, d=64, b=64, T=4, HW=640, G=4, r=0, mask_kind="identity"))
+    w = inp["workload"]
+    res = run_path(inp)
+    g, u, dev = res["g"], res["union"], res["dev"]
+    ranges = bsa.segment_ranges(u.seg_offsets.cpu().numpy(), w.H, w.G)
+    O_run = torch.full_like(res["O"], 7.0)
+    lse_run = torch.full_like(res["lse"], 3.0)
+    for p in range(1, w.G):                      # identity mask: rank 0's rows select only rank 0's blocks
+        lo, hi = ranges[p]
+        assert lo == hi
+        bsa.block_sparse_attn_segment_accumulate(g, dev["Q"], dev["mask"], u.slot_of, res["packed"], lo, hi,
+                                                 O_run, lse_run)
+    bsa.block_sparse_attn_segment_accumulate(g, dev["Q"], dev["mask"], u.slot_of, res["packed"], 0, 0, O_run, lse_run)
+    torch.cuda.synchronize()
+    assert torch.all(O_run == 7.0) and torch.all(lse_run == 3.0)
