@@ -23,11 +23,15 @@ from collections import defaultdict
 
 
 def short_name(name: str) -> str:
-    m = re.search(r"::(\w+_kernel)\b", name)
+    """A kernel's short name: torch's elementwise kernels and the runtime's copy/fill kernels by their
+    family, this library's kernels by their name, anything else by its first name token."""
+    m = re.search(r"(\w*elementwise\w*|__amd_rocclr_\w+)", name)
     if m:
         return m.group(1)
-    m = re.search(r"(\w*elementwise\w*|copyBuffer\w*|\w+)", name)
-    return m.group(1) if m else name[:40]
+    m = re.search(r"(\w+_kernel)\b", name)
+    if m:
+        return m.group(1)
+    return re.sub(r"^void\s+", "", name).split("(")[0].split("<")[0][:40]
 
 
 def _rows(path: str) -> list[dict]:
