@@ -318,3 +318,18 @@ def test_segment_accumulate_leaves_untouched_rows(require_gpu):
     bsa.block_sparse_attn_segment_accumulate(g, dev["Q"], dev["mask"], u.slot_of, res["packed"], 0, 0, O_run, lse_run)
     torch.cuda.synchronize()
     assert torch.all(O_run == 7.0) and torch.all(lse_run == 3.0)
+
+
+def test_maximum_blocks(require_gpu):
+    """nb = 16384 (the library's limit) with 16 ranks under periodic placement: union, compaction and the
+    pack bit-exact; attention on sampled query blocks (first, last, heaviest, lightest, random)."""
+    from _gpu import run_path, to_host_u16, union_host
+    w = custom(H=1, d=64, b=64, T=16, HW=65536, G=16, r=5, placement="periodic", density=0.002)
+    assert w.nb == 16384
+    inp = make_inputs(w)
+    print(f"[parity] maximum blocks: nb={w.nb} Lq={len(inp['q_blocks'])}", flush=True)
+    res = run_path(inp)
+    c = _check_union(union_host(res["union"]), inp)
+    assert np.array_equal(to_host_u16(res["packed"][:c["S"]]),
+                          O.pack(inp["K"], inp["V"], c["slot_block"], c["slot_head"], w.b))
+    _check_attention(inp, res["O"].cpu().numpy(), res["lse"].cpu().numpy(), _sample_items(inp, n_rand=4))
