@@ -103,18 +103,17 @@ __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qp
   for (int i = t; i < pitch; i += NT) sel[i] = 0;
   __syncthreads();
 
-  // Bitonic sort, ascending, of np2 keys (np2 a power of two).
+  // Bitonic sort, ascending, of np2 keys (np2 a power of two); every thread takes whole compare pairs.
   for (int size = 2; size <= np2; size <<= 1)
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = t; i < np2; i += NT) {
-        const int p = i ^ stride;
-        if (p > i) {
-          const uint64_t a = keys[i], b = keys[p];
-          const bool up = (i & size) == 0;
-          if ((a > b) == up) {
-            keys[i] = b;
-            keys[p] = a;
-          }
+      for (int q = t; q < np2 / 2; q += NT) {
+        const int i = ((q & ~(stride - 1)) << 1) | (q & (stride - 1));
+        const int p = i + stride;
+        const uint64_t a = keys[i], b = keys[p];
+        const bool up = (i & size) == 0;
+        if ((a > b) == up) {
+          keys[i] = b;
+          keys[p] = a;
         }
       }
       __syncthreads();
