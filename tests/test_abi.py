@@ -223,3 +223,27 @@ def test_materialize_argument_checks():
     assert mm(gp, FAKE + 4, FAKE, 0.1, 0.5, 1, FAKE, 64, None) == E                      # misaligned
     big = _geom(b=64, N=64 * 4097, Lq=1)
     assert mm(ctypes.byref(big), FAKE, FAKE, 0.1, 0.5, 1, FAKE, 4160, None) == U          # nb > 4096
+
+
+def test_product_path_never_touches_the_oracle():
+    """The HIP library's sources and the Python binding name nothing under oracle/ (the oracle is test
+    infrastructure; the product path has no CPU fallback)."""
+    pkg = os.path.join(ROOT, "block_sparse_attention_rank_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), fn
+                assert "sparsp_oracle" not in text, fn
+    assert "oracle" not in open(HEADER).read().lower()
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """With the library path pointing at nothing, loading raises instead of falling back."""
+    import subprocess
+    import sys
+    code = ("import block_sparse_attention_rank_amd as b\n"
+            "try:\n    b.load()\nexcept RuntimeError as e:\n    print('raised', 'missing' in str(e))\n")
+    env = dict(os.environ, SPARSP_LIB=str(tmp_path / "nope.so"))
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True)
+    assert out.stdout.strip() == "raised True", out.stdout + out.stderr
