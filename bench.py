@@ -406,7 +406,8 @@ def main():
             "H": g.H, "d": g.d, "b": g.b, "N": g.N, "nb": g.nb, "G": g.G, "r": g.r, "Lq": Lq,
             "placement": w.placement, "selected_tiles": pairs,
             "density": round(pairs / (g.H * Lq * g.nb), 4),
-            "slots_S": S, "wire_slots": S - (own_hi - own_lo), "wire_bytes": (S - (own_hi - own_lo)) * slot_bytes,
+            "slots_S": S, "union_fraction": round(S / (g.H * g.nb), 4),
+            "wire_slots": S - (own_hi - own_lo), "wire_bytes": (S - (own_hi - own_lo)) * slot_bytes,
         },
         "components": {
             "union_compact_us": round(t_union * 1e3, 2),
