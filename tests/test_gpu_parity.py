@@ -333,3 +333,25 @@ def test_maximum_blocks(require_gpu):
     assert np.array_equal(to_host_u16(res["packed"][:c["S"]]),
                           O.pack(inp["K"], inp["V"], c["slot_block"], c["slot_head"], w.b))
     _check_attention(inp, res["O"].cpu().numpy(), res["lse"].cpu().numpy(), _sample_items(inp, n_rand=4))
+
+
+def test_segment_accumulate_is_deterministic(require_gpu):
+    """Folding the same segments in the same order twice gives bit-identical (O, lse)."""
+    import torch
+    import block_sparse_attention_rank_amd as bsa
+    from _gpu import run_path
+    inp = make_inputs(custom(H=3, d=128, b=128, T=3, HW=1000, G=4, r=1, density=0.4))
+    w = inp["workload"]
+    res = run_path(inp)
+    g, u, dev = res["g"], res["union"], res["dev"]
+    ranges = bsa.segment_ranges(u.seg_offsets.cpu().numpy(), w.H, w.G)
+    outs = []
+    for _ in range(2):
+        O_run = torch.zeros_like(res["O"])
+        lse_run = torch.full_like(res["lse"], float("-inf"))
+        for p in [(w.r + k) % w.G for k in range(w.G)]:
+            bsa.block_sparse_attn_segment_accumulate(g, dev["Q"], dev["mask"], u.slot_of, res["packed"], *ranges[p],
+                                                     O_run, lse_run)
+        torch.cuda.synchronize()
+        outs.append((O_run.cpu().numpy(), lse_run.cpu().numpy()))
+    assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
