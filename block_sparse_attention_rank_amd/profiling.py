@@ -147,6 +147,10 @@ def traffic(fetch_dir: str, write_dir: str, warmup: int, steps: int, workload: s
 
 
 def attn_counters(pmc_dir: str, warmup: int, steps: int) -> str:
+    """Utilisation of the single-pass bsa_fwd_kernel launches from whichever of these counters the pass
+    collected: MFMA busy and LDS busy / conflicts (SQ_VALU_MFMA_BUSY_CYCLES, SQ_LDS_IDX_ACTIVE,
+    SQ_LDS_BANK_CONFLICT), or the VALU mix (SQ_INSTS_VALU, SQ_INSTS_MFMA, SQ_ACTIVE_INST_VALU); all with
+    GRBM_GUI_ACTIVE for the clock."""
     rows = _rows(_find(pmc_dir, "counter_collection.csv"))
     per = defaultdict(lambda: defaultdict(float))
     dur = {}
@@ -156,16 +160,29 @@ def attn_counters(pmc_dir: str, warmup: int, steps: int) -> str:
         d = int(r["Dispatch_Id"])
         per[d][r["Counter_Name"]] += float(r["Counter_Value"])
         dur[d] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-    out = ["| dispatch | duration us | clock GHz | MFMA busy | LDS busy | LDS conflicts / access |",
-           "|---|---|---|---|---|---|"]
+    valu_mix = any("SQ_INSTS_VALU" in per[d] for d in per)
+    if valu_mix:
+        out = ["| dispatch | duration us | clock GHz | VALU instructions per MFMA | VALU busy | MFMA busy |",
+               "|---|---|---|---|---|---|"]
+    else:
+        out = ["| dispatch | duration us | clock GHz | MFMA busy | LDS busy | LDS conflicts / access |",
+               "|---|---|---|---|---|---|"]
     for d in sorted(per)[:warmup + steps]:
         c = per[d]
         active = c["GRBM_GUI_ACTIVE"] / 8.0
         clock = active / (dur[d] * 1e3)
         mfma = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (active * 1024)
-        lds = c["SQ_LDS_IDX_ACTIVE"] / (active * 256)
-        conf = c["SQ_LDS_BANK_CONFLICT"] / max(1.0, c["SQ_LDS_IDX_ACTIVE"] - c["SQ_LDS_BANK_CONFLICT"])
-        out.append(f"| {d} | {dur[d]:.1f} | {clock:.3f} | {mfma:.3f} | {lds:.3f} | {conf:.3f} |")
+        if valu_mix:
+            # SQ_INSTS_VALU counts MFMAs among the VALU instructions; SQ_ACTIVE_INST_VALU is per wave, in
+            # quad-cycles, summed over all waves: divided by active cycles x 1024 SIMDs it is the busy share
+            # of a SIMD's VALU issue summed over its waves
+            ratio = (c["SQ_INSTS_VALU"] - c["SQ_INSTS_MFMA"]) / max(1.0, c["SQ_INSTS_MFMA"])
+            vbusy = 4 * c["SQ_ACTIVE_INST_VALU"] / (active * 1024)
+            out.append(f"| {d} | {dur[d]:.1f} | {clock:.3f} | {ratio:.2f} | {vbusy:.3f} | {mfma:.3f} |")
+        else:
+            lds = c["SQ_LDS_IDX_ACTIVE"] / (active * 256)
+            conf = c["SQ_LDS_BANK_CONFLICT"] / max(1.0, c["SQ_LDS_IDX_ACTIVE"] - c["SQ_LDS_BANK_CONFLICT"])
+            out.append(f"| {d} | {dur[d]:.1f} | {clock:.3f} | {mfma:.3f} | {lds:.3f} | {conf:.3f} |")
     return "\n".join(out)
 
 
