@@ -104,20 +104,30 @@ __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qp
   __syncthreads();
 
   // Bitonic sort, ascending, of np2 keys (np2 a power of two); every thread takes whole compare pairs.
-  for (int size = 2; size <= np2; size <<= 1)
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int q = t; q < np2 / 2; q += NT) {
-        const int i = ((q & ~(stride - 1)) << 1) | (q & (stride - 1));
-        const int p = i + stride;
-        const uint64_t a = keys[i], b = keys[p];
-        const bool up = (i & size) == 0;
-        if ((a > b) == up) {
-          keys[i] = b;
-          keys[p] = a;
-        }
+  // A pass of stride s < 64 keeps each wave inside its own 128-key chunks (pair q of a wave's 64 maps into
+  // chunk q / 64), so the passes of stride 32 .. 1 of one merge size run back to back without a workgroup
+  // barrier: a wave's LDS accesses complete in order.  Larger strides cross waves and end in a barrier.
+  auto pass = [&](int size, int stride) {
+    for (int q = t; q < np2 / 2; q += NT) {
+      const int i = ((q & ~(stride - 1)) << 1) | (q & (stride - 1));
+      const int p = i + stride;
+      const uint64_t a = keys[i], b = keys[p];
+      const bool up = (i & size) == 0;
+      if ((a > b) == up) {
+        keys[i] = b;
+        keys[p] = a;
       }
+    }
+  };
+  for (int size = 2; size <= np2; size <<= 1) {
+    int stride = size >> 1;
+    for (; stride >= 64; stride >>= 1) {
+      pass(size, stride);
       __syncthreads();
     }
+    for (; stride > 0; stride >>= 1) pass(size, stride);
+    __syncthreads();
+  }
 
   // Softmax weights in sorted order and their inclusive prefix sums.  Each thread scans a run of
   // consecutive entries; the runs' totals are scanned across the workgroup in thread order.
