@@ -310,8 +310,6 @@ int32_t sparsp_materialize_mask(const sparsp_geometry* geom, const float* q_pool
   if (!q_pooled || !k_pooled) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
   if (!aligned16(q_pooled) || !aligned16(k_pooled))
     return fail(SPARSP_ERR_INVALID, fn, "q_pooled and k_pooled must be 16-byte aligned");
-  if (mask_pitch > 16384 || sparsp::select_lds_bytes(d.nb, d.d, mask_pitch) > 65536)
-    return fail(SPARSP_ERR_UNSUPPORTED, fn, "mask_pitch too large for one workgroup's LDS");
   return hip_status(sparsp::launch_select(d, q_pooled, k_pooled, softmax_scale, tau, k_min, mask, mask_pitch,
                                           reinterpret_cast<hipStream_t>(stream)),
                     fn);

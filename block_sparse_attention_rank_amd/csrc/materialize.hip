@@ -6,12 +6,14 @@
 // 16-byte loads, fp32 sums, row groups combined through LDS in a fixed order).  HBM-bound: it reads
 // every token of K once.
 //
-// select_kernel: one workgroup per (head, local query block).  Block scores s_j = scale <q, k_j> against
-// every pooled key; the (score, block) pairs are sorted in LDS by a bitonic network into descending
-// score order (equal scores: ascending block); the softmax weights exp(s - max) are prefix-summed in
-// that order; the row keeps the smallest prefix holding at least tau of the mass, but at least k_min
-// blocks (a Top-p rule with a Top-k floor), and writes the uint8 mask row the demand union and the
-// attention consume.
+// select_kernel: one workgroup per (head, local query block); every thread keeps up to four of the row's
+// blocks in registers.  Block scores s_j = scale <q, k_j> against every pooled key are keyed so that
+// ascending key order is descending score (equal scores: ascending block); the softmax weights exp(s - max)
+// are summed, and the smallest key threshold whose blocks hold at least tau of the weight is found bit by
+// bit with workgroup reductions in a fixed order (no sort); a second, count-only search applies the Top-k
+// floor k_min.  The row keeps the blocks at or below the threshold (a Top-p rule with a Top-k floor) and
+// writes the uint8 mask row the demand union and the attention consume.  Integer counts and fixed-order
+// fp32 sums make the result deterministic.
 #include <math.h>
 
 #include "sparsp_internal.h"
@@ -58,6 +60,13 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(const uint16_t* __re
   }
 }
 
+// 64-bit lane exchange: the value of lane (this lane ^ m).
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const unsigned lo = (unsigned)__shfl_xor((int)(uint32_t)v, m, 64);
+  const unsigned hi = (unsigned)__shfl_xor((int)(uint32_t)(v >> 32), m, 64);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Monotone map of a float to an unsigned key (larger float -> larger key).
 __device__ __forceinline__ uint32_t ordered_bits(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -68,27 +77,33 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-// NT threads: 256 for rows of up to 1024 blocks, 1024 above (the sort's passes are separated by barriers,
-// so more threads per row shorten every pass).
+// NT threads: 256 for rows of up to 1024 blocks, 1024 above; each thread keeps PER = np2 / NT <= 4 of the
+// row's blocks in registers.
 template <int D, int NT>
 __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qp, const float* __restrict__ kp,
-                                                                int Lq, int nb, int np2, float scale, float tau,
-                                                                int k_min, uint8_t* __restrict__ mask, int64_t pitch) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);        // [np2]
-  float* cum = reinterpret_cast<float*>(keys + np2);          // [np2]
-  float* qv = cum + np2;                                      // [D]
-  int* wsum = reinterpret_cast<int*>(qv + D);                 // scan scratch: one entry per wave (<= 16)
-  uint8_t* sel = reinterpret_cast<uint8_t*>(wsum + 16);       // [pitch]
+                                                    int Lq, int nb, int np2, float scale, float tau, int k_min,
+                                                    uint8_t* __restrict__ mask, int64_t pitch) {
+  constexpr int PER = 4;
+  constexpr int NWV = NT / 64;
+  __shared__ float qv[D];
+  __shared__ float fbuf[2][NWV];
+  __shared__ int ibuf[2][NWV];
+  __shared__ uint64_t kbuf[NWV];
 
   const int k = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int lane = t % 64, wave = t / 64;
   if (t < D) qv[t] = qp[((int64_t)h * Lq + k) * D + t];
   __syncthreads();
 
-  // Scores, keyed so that an ascending sort gives descending score and, among equal scores, ascending j.
+  // Keys of this thread's blocks j = t + r NT: ascending key = descending score, equal scores by ascending j;
+  // positions past nb get the largest key and no weight.
   const float4* kh = reinterpret_cast<const float4*>(kp + (int64_t)h * nb * D);
-  for (int j = t; j < np2; j += NT) {
-    uint64_t key = ~0ull;
+  uint64_t key[PER];
+  float w[PER];
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int j = t + r * NT;
+    key[r] = ~0ull;
     if (j < nb) {
       float s = 0.f;
 #pragma unroll 8
@@ -96,83 +111,98 @@ __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qp
         const float4 kv = kh[(int64_t)j * (D / 4) + c];
         s += qv[4 * c] * kv.x + qv[4 * c + 1] * kv.y + qv[4 * c + 2] * kv.z + qv[4 * c + 3] * kv.w;
       }
-      key = ((uint64_t)(~ordered_bits(s * scale)) << 32) | (uint32_t)j;
+      key[r] = ((uint64_t)(~ordered_bits(s * scale)) << 32) | (uint32_t)j;
     }
-    keys[j] = key;
   }
-  for (int i = t; i < pitch; i += NT) sel[i] = 0;
-  __syncthreads();
 
-  // Bitonic sort, ascending, of np2 keys (np2 a power of two); every thread takes whole compare pairs.
-  // A pass of stride s < 64 keeps each wave inside its own 128-key chunks (pair q of a wave's 64 maps into
-  // chunk q / 64), so the passes of stride 32 .. 1 of one merge size run back to back without a workgroup
-  // barrier: a wave's LDS accesses complete in order.  Larger strides cross waves and end in a barrier.
-  auto pass = [&](int size, int stride) {
-    for (int q = t; q < np2 / 2; q += NT) {
-      const int i = ((q & ~(stride - 1)) << 1) | (q & (stride - 1));
-      const int p = i + stride;
-      const uint64_t a = keys[i], b = keys[p];
-      const bool up = (i & size) == 0;
-      if ((a > b) == up) {
-        keys[i] = b;
-        keys[p] = a;
-      }
-    }
-  };
-  for (int size = 2; size <= np2; size <<= 1) {
-    int stride = size >> 1;
-    for (; stride >= 64; stride >>= 1) {
-      pass(size, stride);
-      __syncthreads();
-    }
-    for (; stride > 0; stride >>= 1) pass(size, stride);
+  // Workgroup reductions in a fixed order (deterministic): butterfly within the wave, then the waves' totals
+  // in wave order.  Two alternating LDS buffers let one barrier separate consecutive reductions.
+  int parity = 0;
+  auto sum_f = [&](float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) fbuf[parity][wave] = v;
     __syncthreads();
-  }
-
-  // Softmax weights in sorted order and their inclusive prefix sums.  Each thread scans a run of
-  // consecutive entries; the runs' totals are scanned across the workgroup in thread order.
-  const float smax = from_ordered_bits(~(uint32_t)(keys[0] >> 32));
-  const int per = (np2 + NT - 1) / NT;
-  const int i0 = t * per;
-  float run = 0.f;
-  for (int i = i0; i < min(i0 + per, nb); ++i) {
-    run += expf(from_ordered_bits(~(uint32_t)(keys[i] >> 32)) - smax);
-    cum[i] = run;
-  }
-  // exclusive scan of the run totals: within the wave by shuffles, then across the waves through LDS
-  const int lane = t % 64, wave = t / 64;
-  float incl = run;
+    float tot = 0.f;
 #pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  float* wtot = reinterpret_cast<float*>(wsum);
-  if (lane == 63) wtot[wave] = incl;
-  __syncthreads();
-  float base = incl - run;
-  for (int w = 0; w < wave; ++w) base += wtot[w];
-  for (int i = i0; i < min(i0 + per, nb); ++i) cum[i] += base;
-  __syncthreads();
-
-  // n_tau = 1 + the number of prefixes still short of tau of the total mass (cum is nondecreasing).
-  const float target = tau * cum[nb - 1];
-  int below = 0;
-  for (int i = t; i < nb; i += NT) below += cum[i] < target ? 1 : 0;
+    for (int x = 0; x < NWV; ++x) tot += fbuf[parity][x];
+    parity ^= 1;
+    return tot;
+  };
+  auto sum_i = [&](int v) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) below += __shfl_xor(below, off, 64);
-  __syncthreads();
-  if (lane == 0) wsum[wave] = below;
-  __syncthreads();
-  int n_tau = 1;
-  for (int w = 0; w < NT / 64; ++w) n_tau += wsum[w];
-  const int n = min(nb, max(k_min, n_tau));
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if (lane == 0) ibuf[parity][wave] = v;
+    __syncthreads();
+    int tot = 0;
+#pragma unroll
+    for (int x = 0; x < NWV; ++x) tot += ibuf[parity][x];
+    parity ^= 1;
+    return tot;
+  };
 
-  for (int i = t; i < n; i += NT) sel[(uint32_t)keys[i]] = 1;
+  // The smallest key is the row's maximum score.
+  uint64_t kmin = key[0];
+#pragma unroll
+  for (int r = 1; r < PER; ++r) kmin = key[r] < kmin ? key[r] : kmin;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint64_t o = shfl_xor64(kmin, off);
+    kmin = o < kmin ? o : kmin;
+  }
+  if (lane == 0) kbuf[wave] = kmin;
   __syncthreads();
+  kmin = kbuf[0];
+  for (int x = 1; x < NWV; ++x) kmin = kbuf[x] < kmin ? kbuf[x] : kmin;
+  const float smax = from_ordered_bits(~(uint32_t)(kmin >> 32));
+
+  float part = 0.f;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    w[r] = key[r] != ~0ull ? expf(from_ordered_bits(~(uint32_t)(key[r] >> 32)) - smax) : 0.f;
+    part += w[r];
+  }
+  const float target = tau * sum_f(part);
+
+  // The smallest key threshold T whose blocks (key <= T) hold at least tau of the weight, found bit by bit
+  // (bits 63..32: the score, bits 11..0: the block; no key has bits 31..12 set); n_tau = |{key <= T}|, at
+  // least 1.
+  auto mass_le = [&](uint64_t T) {
+    float m = 0.f;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) m += key[r] <= T ? w[r] : 0.f;
+    return sum_f(m);
+  };
+  auto count_le = [&](uint64_t T) {
+    int c = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) c += key[r] <= T ? 1 : 0;
+    return sum_i(c);
+  };
+  uint64_t T = 0;
+  for (int bit = 63; bit >= 0; --bit) {
+    if (bit == 31) bit = 11;
+    const uint64_t probe = T | ((1ull << bit) - 1ull);
+    if (!(mass_le(probe) >= target)) T |= 1ull << bit;
+  }
+  int cnt = count_le(T);
+  const int n = min(nb, max(k_min, max(1, cnt)));
+  if (n > cnt) {  // the Top-k floor (or the first block) asks for more: the n-th smallest key
+    T = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      if (bit == 31) bit = 11;
+      const uint64_t probe = T | ((1ull << bit) - 1ull);
+      if (count_le(probe) < n) T |= 1ull << bit;
+    }
+  }
+
   uint8_t* row = mask + ((int64_t)h * Lq + k) * pitch;
-  for (int i = t * 16; i < pitch; i += NT * 16)
-    *reinterpret_cast<uint4*>(row + i) = *reinterpret_cast<const uint4*>(sel + i);
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int j = t + r * NT;
+    if (j < pitch) row[j] = (j < nb && key[r] <= T) ? 1 : 0;
+  }
+  for (int i = np2 + t; i < pitch; i += NT) row[i] = 0;
 }
 
 template <int D>
@@ -188,13 +218,6 @@ hipError_t launch_pool_d(const Dims& g, const uint16_t* X, int n_blocks, const i
 
 }  // namespace
 
-// Sort size: a power of two >= nb, at least 4 so that the selection bytes start 16-byte aligned.
-size_t select_lds_bytes(int nb, int d, int64_t pitch) {
-  int np2 = 4;
-  while (np2 < nb) np2 <<= 1;
-  return (size_t)np2 * 12 + (size_t)d * 4 + 64 + (size_t)pitch;
-}
-
 hipError_t launch_pool(const Dims& g, const uint16_t* X, int n_blocks, const int32_t* block_ids, float* pooled,
                        hipStream_t stream) {
   if (n_blocks == 0) return hipSuccess;
@@ -205,9 +228,9 @@ hipError_t launch_pool(const Dims& g, const uint16_t* X, int n_blocks, const int
 hipError_t launch_select(const Dims& g, const float* q_pooled, const float* k_pooled, float scale, float tau,
                          int k_min, uint8_t* mask, int64_t pitch, hipStream_t stream) {
   if (g.Lq == 0) return hipSuccess;
-  int np2 = 4;
+  int np2 = 4;  // row length rounded up to a power of two
   while (np2 < g.nb) np2 <<= 1;
-  const size_t lds = select_lds_bytes(g.nb, g.d, pitch);
+  const size_t lds = 0;
   const dim3 grid((unsigned)g.Lq, (unsigned)g.H);
   const bool wide = np2 > 1024;
   if (g.d == 128 && wide)

@@ -48,7 +48,6 @@ hipError_t launch_pool(const Dims& g, const uint16_t* X, int n_blocks, const int
 // Mask rows [H][Lq][pitch] from pooled tiles: Top-p (tau) with a Top-k floor (k_min) over the block scores.
 hipError_t launch_select(const Dims& g, const float* q_pooled, const float* k_pooled, float scale, float tau,
                          int k_min, uint8_t* mask, int64_t pitch, hipStream_t stream);
-size_t select_lds_bytes(int nb, int d, int64_t pitch);
 constexpr int kMaxSelectBlocks = 4096;
 
 // Move whole blocks: dst[o][pos[j]] = src[o][j] (inverse = 0) or dst[o][j] = src[o][pos[j]] (inverse = 1).
