@@ -6,14 +6,15 @@
 // 16-byte loads, fp32 sums, row groups combined through LDS in a fixed order).  HBM-bound: it reads
 // every token of K once.
 //
-// select_kernel: one workgroup per (head, local query block); every thread keeps up to four of the row's
-// blocks in registers.  Block scores s_j = scale <q, k_j> against every pooled key are keyed so that
-// ascending key order is descending score (equal scores: ascending block); the softmax weights exp(s - max)
-// are summed, and the smallest key threshold whose blocks hold at least tau of the weight is found bit by
-// bit with workgroup reductions in a fixed order (no sort); a second, count-only search applies the Top-k
-// floor k_min.  The row keeps the blocks at or below the threshold (a Top-p rule with a Top-k floor) and
-// writes the uint8 mask row the demand union and the attention consume.  Integer counts and fixed-order
-// fp32 sums make the result deterministic.
+// select_kernel: one workgroup per (head, R consecutive local query blocks); every thread keeps up to four
+// of each row's blocks in registers, and the R rows share every pooled-key read and every reduction.  Block
+// scores s_j = scale <q, k_j> against every pooled key are keyed so that ascending key order is descending
+// score (equal scores: ascending block); the softmax weights exp(s - max) are summed, and the smallest key
+// threshold whose blocks hold at least tau of the weight is found bit by bit with workgroup reductions in
+// a fixed order (no sort); a second, count-only search applies the Top-k floor k_min.  A row keeps the
+// blocks at or below its threshold (a Top-p rule with a Top-k floor) and writes the uint8 mask row the
+// demand union and the attention consume.  Integer counts and fixed-order fp32 sums make the result
+// deterministic.
 #include <math.h>
 
 #include "sparsp_internal.h"
@@ -77,132 +78,195 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-// NT threads: 256 for rows of up to 1024 blocks, 1024 above; each thread keeps PER = np2 / NT <= 4 of the
-// row's blocks in registers.
-template <int D, int NT>
+// NT threads: 256 for rows of up to 1024 blocks, 1024 above; each thread keeps PER = np2 / NT <= 4 blocks of
+// each of the workgroup's R rows in registers.  The R rows (consecutive local query blocks of one head) share
+// every pooled-key read and every reduction.
+template <int D, int NT, int R>
 __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qp, const float* __restrict__ kp,
                                                     int Lq, int nb, int np2, float scale, float tau, int k_min,
                                                     uint8_t* __restrict__ mask, int64_t pitch) {
   constexpr int PER = 4;
   constexpr int NWV = NT / 64;
-  __shared__ float qv[D];
-  __shared__ float fbuf[2][NWV];
-  __shared__ int ibuf[2][NWV];
-  __shared__ uint64_t kbuf[NWV];
+  __shared__ float qv[R][D];
+  __shared__ float fbuf[2][R][NWV];
+  __shared__ int ibuf[2][R][NWV];
+  __shared__ uint64_t kbuf[R][NWV];
 
-  const int k = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int k0 = blockIdx.x * R, h = blockIdx.y, t = threadIdx.x;
   const int lane = t % 64, wave = t / 64;
-  if (t < D) qv[t] = qp[((int64_t)h * Lq + k) * D + t];
+  for (int i = t; i < R * D; i += NT) {
+    const int rr = i / D, k = min(k0 + rr, Lq - 1);  // rows past Lq repeat the last one and are not written
+    qv[rr][i % D] = qp[((int64_t)h * Lq + k) * D + i % D];
+  }
   __syncthreads();
 
   // Keys of this thread's blocks j = t + r NT: ascending key = descending score, equal scores by ascending j;
   // positions past nb get the largest key and no weight.
   const float4* kh = reinterpret_cast<const float4*>(kp + (int64_t)h * nb * D);
-  uint64_t key[PER];
-  float w[PER];
+  uint64_t key[R][PER];
+  float w[R][PER];
 #pragma unroll
   for (int r = 0; r < PER; ++r) {
     const int j = t + r * NT;
-    key[r] = ~0ull;
+#pragma unroll
+    for (int q = 0; q < R; ++q) key[q][r] = ~0ull;
     if (j < nb) {
-      float s = 0.f;
-#pragma unroll 8
+      float s[R];
+#pragma unroll
+      for (int q = 0; q < R; ++q) s[q] = 0.f;
+#pragma unroll 4
       for (int c = 0; c < D / 4; ++c) {
         const float4 kv = kh[(int64_t)j * (D / 4) + c];
-        s += qv[4 * c] * kv.x + qv[4 * c + 1] * kv.y + qv[4 * c + 2] * kv.z + qv[4 * c + 3] * kv.w;
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+          s[q] += qv[q][4 * c] * kv.x + qv[q][4 * c + 1] * kv.y + qv[q][4 * c + 2] * kv.z + qv[q][4 * c + 3] * kv.w;
       }
-      key[r] = ((uint64_t)(~ordered_bits(s * scale)) << 32) | (uint32_t)j;
+#pragma unroll
+      for (int q = 0; q < R; ++q) key[q][r] = ((uint64_t)(~ordered_bits(s[q] * scale)) << 32) | (uint32_t)j;
     }
   }
 
-  // Workgroup reductions in a fixed order (deterministic): butterfly within the wave, then the waves' totals
-  // in wave order.  Two alternating LDS buffers let one barrier separate consecutive reductions.
+  // Workgroup reductions of R values at once, in a fixed order (deterministic): butterfly within the wave,
+  // then the waves' totals in wave order.  Two alternating LDS buffers let one barrier separate
+  // consecutive reductions.
   int parity = 0;
-  auto sum_f = [&](float v) {
+  auto sum_f = [&](float (&v)[R]) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    if (lane == 0) fbuf[parity][wave] = v;
+    for (int q = 0; q < R; ++q) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v[q] += __shfl_xor(v[q], off, 64);
+      if (lane == 0) fbuf[parity][q][wave] = v[q];
+    }
     __syncthreads();
-    float tot = 0.f;
 #pragma unroll
-    for (int x = 0; x < NWV; ++x) tot += fbuf[parity][x];
+    for (int q = 0; q < R; ++q) {
+      float tot = 0.f;
+#pragma unroll
+      for (int x = 0; x < NWV; ++x) tot += fbuf[parity][q][x];
+      v[q] = tot;
+    }
     parity ^= 1;
-    return tot;
   };
-  auto sum_i = [&](int v) {
+  auto sum_i = [&](int (&v)[R]) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-    if (lane == 0) ibuf[parity][wave] = v;
+    for (int q = 0; q < R; ++q) {
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) v[q] += __shfl_xor(v[q], off, 64);
+      if (lane == 0) ibuf[parity][q][wave] = v[q];
+    }
     __syncthreads();
-    int tot = 0;
 #pragma unroll
-    for (int x = 0; x < NWV; ++x) tot += ibuf[parity][x];
+    for (int q = 0; q < R; ++q) {
+      int tot = 0;
+#pragma unroll
+      for (int x = 0; x < NWV; ++x) tot += ibuf[parity][q][x];
+      v[q] = tot;
+    }
     parity ^= 1;
-    return tot;
   };
 
-  // The smallest key is the row's maximum score.
-  uint64_t kmin = key[0];
+  // The smallest key of a row is its maximum score.
+  float target[R];
 #pragma unroll
-  for (int r = 1; r < PER; ++r) kmin = key[r] < kmin ? key[r] : kmin;
+  for (int q = 0; q < R; ++q) {
+    uint64_t kmin = key[q][0];
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const uint64_t o = shfl_xor64(kmin, off);
-    kmin = o < kmin ? o : kmin;
+    for (int r = 1; r < PER; ++r) kmin = key[q][r] < kmin ? key[q][r] : kmin;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const uint64_t o = shfl_xor64(kmin, off);
+      kmin = o < kmin ? o : kmin;
+    }
+    if (lane == 0) kbuf[q][wave] = kmin;
   }
-  if (lane == 0) kbuf[wave] = kmin;
   __syncthreads();
-  kmin = kbuf[0];
-  for (int x = 1; x < NWV; ++x) kmin = kbuf[x] < kmin ? kbuf[x] : kmin;
-  const float smax = from_ordered_bits(~(uint32_t)(kmin >> 32));
-
-  float part = 0.f;
 #pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    w[r] = key[r] != ~0ull ? expf(from_ordered_bits(~(uint32_t)(key[r] >> 32)) - smax) : 0.f;
-    part += w[r];
+  for (int q = 0; q < R; ++q) {
+    uint64_t kmin = kbuf[q][0];
+    for (int x = 1; x < NWV; ++x) kmin = kbuf[q][x] < kmin ? kbuf[q][x] : kmin;
+    const float smax = from_ordered_bits(~(uint32_t)(kmin >> 32));
+    float part = 0.f;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      w[q][r] = key[q][r] != ~0ull ? expf(from_ordered_bits(~(uint32_t)(key[q][r] >> 32)) - smax) : 0.f;
+      part += w[q][r];
+    }
+    target[q] = part;
   }
-  const float target = tau * sum_f(part);
+  sum_f(target);
+#pragma unroll
+  for (int q = 0; q < R; ++q) target[q] *= tau;
 
-  // The smallest key threshold T whose blocks (key <= T) hold at least tau of the weight, found bit by bit
-  // (bits 63..32: the score, bits 11..0: the block; no key has bits 31..12 set); n_tau = |{key <= T}|, at
-  // least 1.
-  auto mass_le = [&](uint64_t T) {
-    float m = 0.f;
+  // Per row, the smallest key threshold T whose blocks (key <= T) hold at least tau of the weight, found bit by
+  // bit (bits 63..32: the score, bits 11..0: the block; no key has bits 31..12 set); n_tau = |{key <= T}|,
+  // at least 1.
+  uint64_t T[R];
 #pragma unroll
-    for (int r = 0; r < PER; ++r) m += key[r] <= T ? w[r] : 0.f;
-    return sum_f(m);
-  };
-  auto count_le = [&](uint64_t T) {
-    int c = 0;
-#pragma unroll
-    for (int r = 0; r < PER; ++r) c += key[r] <= T ? 1 : 0;
-    return sum_i(c);
-  };
-  uint64_t T = 0;
+  for (int q = 0; q < R; ++q) T[q] = 0;
   for (int bit = 63; bit >= 0; --bit) {
     if (bit == 31) bit = 11;
-    const uint64_t probe = T | ((1ull << bit) - 1ull);
-    if (!(mass_le(probe) >= target)) T |= 1ull << bit;
+    float m[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const uint64_t probe = T[q] | ((1ull << bit) - 1ull);
+      m[q] = 0.f;
+#pragma unroll
+      for (int r = 0; r < PER; ++r) m[q] += key[q][r] <= probe ? w[q][r] : 0.f;
+    }
+    sum_f(m);
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+      if (!(m[q] >= target[q])) T[q] |= 1ull << bit;
   }
-  int cnt = count_le(T);
-  const int n = min(nb, max(k_min, max(1, cnt)));
-  if (n > cnt) {  // the Top-k floor (or the first block) asks for more: the n-th smallest key
-    T = 0;
+  int cnt[R], n[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    cnt[q] = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) cnt[q] += key[q][r] <= T[q] ? 1 : 0;
+  }
+  sum_i(cnt);
+  bool more = false;
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    n[q] = min(nb, max(k_min, max(1, cnt[q])));
+    more |= n[q] > cnt[q];
+  }
+  if (more) {  // the Top-k floor (or the first block) asks for more: the n-th smallest key of those rows
+    uint64_t T2[R];
+#pragma unroll
+    for (int q = 0; q < R; ++q) T2[q] = 0;
     for (int bit = 63; bit >= 0; --bit) {
       if (bit == 31) bit = 11;
-      const uint64_t probe = T | ((1ull << bit) - 1ull);
-      if (count_le(probe) < n) T |= 1ull << bit;
+      int c[R];
+#pragma unroll
+      for (int q = 0; q < R; ++q) {
+        const uint64_t probe = T2[q] | ((1ull << bit) - 1ull);
+        c[q] = 0;
+#pragma unroll
+        for (int r = 0; r < PER; ++r) c[q] += key[q][r] <= probe ? 1 : 0;
+      }
+      sum_i(c);
+#pragma unroll
+      for (int q = 0; q < R; ++q)
+        if (c[q] < n[q]) T2[q] |= 1ull << bit;
     }
+#pragma unroll
+    for (int q = 0; q < R; ++q)
+      if (n[q] > cnt[q]) T[q] = T2[q];
   }
 
-  uint8_t* row = mask + ((int64_t)h * Lq + k) * pitch;
 #pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int j = t + r * NT;
-    if (j < pitch) row[j] = (j < nb && key[r] <= T) ? 1 : 0;
+  for (int q = 0; q < R; ++q) {
+    if (k0 + q >= Lq) break;
+    uint8_t* row = mask + ((int64_t)h * Lq + k0 + q) * pitch;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int j = t + r * NT;
+      if (j < pitch) row[j] = (j < nb && key[q][r] <= T[q]) ? 1 : 0;
+    }
+    for (int i = np2 + t; i < pitch; i += NT) row[i] = 0;
   }
-  for (int i = np2 + t; i < pitch; i += NT) row[i] = 0;
 }
 
 template <int D>
@@ -230,21 +294,25 @@ hipError_t launch_select(const Dims& g, const float* q_pooled, const float* k_po
   if (g.Lq == 0) return hipSuccess;
   int np2 = 4;  // row length rounded up to a power of two
   while (np2 < g.nb) np2 <<= 1;
-  const size_t lds = 0;
-  const dim3 grid((unsigned)g.Lq, (unsigned)g.H);
-  const bool wide = np2 > 1024;
-  if (g.d == 128 && wide)
-    hipLaunchKernelGGL((select_kernel<128, 1024>), grid, dim3(1024), lds, stream, q_pooled, k_pooled, g.Lq, g.nb,
-                       np2, scale, tau, k_min, mask, pitch);
-  else if (g.d == 128)
-    hipLaunchKernelGGL((select_kernel<128, 256>), grid, dim3(256), lds, stream, q_pooled, k_pooled, g.Lq, g.nb, np2,
-                       scale, tau, k_min, mask, pitch);
-  else if (wide)
-    hipLaunchKernelGGL((select_kernel<64, 1024>), grid, dim3(1024), lds, stream, q_pooled, k_pooled, g.Lq, g.nb,
-                       np2, scale, tau, k_min, mask, pitch);
-  else
-    hipLaunchKernelGGL((select_kernel<64, 256>), grid, dim3(256), lds, stream, q_pooled, k_pooled, g.Lq, g.nb, np2,
-                       scale, tau, k_min, mask, pitch);
+  // Rows of up to 1024 blocks: 256 threads and four rows per workgroup; longer rows: 1024 threads, one row
+  // (more rows per workgroup measured slower there: the register budget per thread halves).
+  if (np2 <= 1024) {
+    const dim3 grid((unsigned)((g.Lq + 3) / 4), (unsigned)g.H);
+    if (g.d == 128)
+      hipLaunchKernelGGL((select_kernel<128, 256, 4>), grid, dim3(256), 0, stream, q_pooled, k_pooled, g.Lq, g.nb, np2,
+                         scale, tau, k_min, mask, pitch);
+    else
+      hipLaunchKernelGGL((select_kernel<64, 256, 4>), grid, dim3(256), 0, stream, q_pooled, k_pooled, g.Lq, g.nb, np2,
+                         scale, tau, k_min, mask, pitch);
+  } else {
+    const dim3 grid((unsigned)g.Lq, (unsigned)g.H);
+    if (g.d == 128)
+      hipLaunchKernelGGL((select_kernel<128, 1024, 1>), grid, dim3(1024), 0, stream, q_pooled, k_pooled, g.Lq, g.nb,
+                         np2, scale, tau, k_min, mask, pitch);
+    else
+      hipLaunchKernelGGL((select_kernel<64, 1024, 1>), grid, dim3(1024), 0, stream, q_pooled, k_pooled, g.Lq, g.nb,
+                         np2, scale, tau, k_min, mask, pitch);
+  }
   return hipGetLastError();
 }
 
