@@ -68,6 +68,32 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Sum over the 64 lanes of a wave, the same in every lane, in a fixed order (deterministic): DPP steps within
+// quads, half-rows and rows of 16, then the row broadcasts of lanes 15 and 31 gather the four rows into lane
+// 63, which is read back.  Needs all 64 lanes active.
+template <int Ctrl, int RowMask>
+__device__ __forceinline__ int dpp_step(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, Ctrl, RowMask, 0xF, false);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __int_as_float(dpp_step<0xB1, 0xF>(__float_as_int(v)));   // quad_perm [1, 0, 3, 2]
+  v += __int_as_float(dpp_step<0x4E, 0xF>(__float_as_int(v)));   // quad_perm [2, 3, 0, 1]
+  v += __int_as_float(dpp_step<0x141, 0xF>(__float_as_int(v)));  // row_half_mirror
+  v += __int_as_float(dpp_step<0x140, 0xF>(__float_as_int(v)));  // row_mirror
+  v += __int_as_float(dpp_step<0x142, 0xA>(__float_as_int(v)));  // row_bcast:15 into rows 1 and 3
+  v += __int_as_float(dpp_step<0x143, 0xC>(__float_as_int(v)));  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ int wave_sum(int v) {
+  v += dpp_step<0xB1, 0xF>(v);
+  v += dpp_step<0x4E, 0xF>(v);
+  v += dpp_step<0x141, 0xF>(v);
+  v += dpp_step<0x140, 0xF>(v);
+  v += dpp_step<0x142, 0xA>(v);
+  v += dpp_step<0x143, 0xC>(v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
 // Monotone map of a float to an unsigned key (larger float -> larger key).
 __device__ __forceinline__ uint32_t ordered_bits(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -126,16 +152,15 @@ __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qp
     }
   }
 
-  // Workgroup reductions of R values at once, in a fixed order (deterministic): butterfly within the wave,
-  // then the waves' totals in wave order.  Two alternating LDS buffers let one barrier separate
+  // Workgroup reductions of R values at once, in a fixed order (deterministic): DPP within the wave, then the
+  // waves' totals in wave order.  Two alternating LDS buffers let one barrier separate
   // consecutive reductions.
   int parity = 0;
   auto sum_f = [&](float (&v)[R]) {
 #pragma unroll
     for (int q = 0; q < R; ++q) {
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) v[q] += __shfl_xor(v[q], off, 64);
-      if (lane == 0) fbuf[parity][q][wave] = v[q];
+      const float ws = wave_sum(v[q]);
+      if (lane == 0) fbuf[parity][q][wave] = ws;
     }
     __syncthreads();
 #pragma unroll
@@ -150,9 +175,8 @@ __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qp
   auto sum_i = [&](int (&v)[R]) {
 #pragma unroll
     for (int q = 0; q < R; ++q) {
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) v[q] += __shfl_xor(v[q], off, 64);
-      if (lane == 0) ibuf[parity][q][wave] = v[q];
+      const int ws = wave_sum(v[q]);
+      if (lane == 0) ibuf[parity][q][wave] = ws;
     }
     __syncthreads();
 #pragma unroll
@@ -198,13 +222,14 @@ __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qp
   for (int q = 0; q < R; ++q) target[q] *= tau;
 
   // Per row, the smallest key threshold T whose blocks (key <= T) hold at least tau of the weight, found bit by
-  // bit (bits 63..32: the score, bits 11..0: the block; no key has bits 31..12 set); n_tau = |{key <= T}|,
-  // at least 1.
+  // bit (bits 63..32: the score, then the low bits a block index below np2 can have; no key has the bits in
+  // between set); n_tau = |{key <= T}|, at least 1.
+  const int jbits = 31 - __clz(np2);  // index bits a block of this row can have set
   uint64_t T[R];
 #pragma unroll
   for (int q = 0; q < R; ++q) T[q] = 0;
   for (int bit = 63; bit >= 0; --bit) {
-    if (bit == 31) bit = 11;
+    if (bit == 31) bit = jbits - 1;
     float m[R];
 #pragma unroll
     for (int q = 0; q < R; ++q) {
@@ -230,6 +255,10 @@ __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qp
 #pragma unroll
   for (int q = 0; q < R; ++q) {
     n[q] = min(nb, max(k_min, max(1, cnt[q])));
+    if (n[q] == nb && cnt[q] < nb) {  // every block: no search needed
+      T[q] = ~0ull;
+      cnt[q] = nb;
+    }
     more |= n[q] > cnt[q];
   }
   if (more) {  // the Top-k floor (or the first block) asks for more: the n-th smallest key of those rows
@@ -237,7 +266,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qp
 #pragma unroll
     for (int q = 0; q < R; ++q) T2[q] = 0;
     for (int bit = 63; bit >= 0; --bit) {
-      if (bit == 31) bit = 11;
+      if (bit == 31) bit = jbits - 1;
       int c[R];
 #pragma unroll
       for (int q = 0; q < R; ++q) {
