@@ -104,14 +104,13 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
   return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-// NT threads: 256 for rows of up to 1024 blocks, 1024 above; each thread keeps PER = np2 / NT <= 4 blocks of
-// each of the workgroup's R rows in registers.  The R rows (consecutive local query blocks of one head) share
-// every pooled-key read and every reduction.
-template <int D, int NT, int R>
+// NT threads, each keeping PER >= np2 / NT blocks of each of the workgroup's R rows in registers: 256 threads,
+// four blocks and four rows for rows of up to 1024 blocks; 512 threads, eight blocks and two rows above.  The
+// R rows (consecutive local query blocks of one head) share every pooled-key read and every reduction.
+template <int D, int NT, int R, int PER>
 __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qp, const float* __restrict__ kp,
                                                     int Lq, int nb, int np2, float scale, float tau, int k_min,
                                                     uint8_t* __restrict__ mask, int64_t pitch) {
-  constexpr int PER = 4;
   constexpr int NWV = NT / 64;
   __shared__ float qv[R][D];
   __shared__ float fbuf[2][R][NWV];
@@ -323,23 +322,24 @@ hipError_t launch_select(const Dims& g, const float* q_pooled, const float* k_po
   if (g.Lq == 0) return hipSuccess;
   int np2 = 4;  // row length rounded up to a power of two
   while (np2 < g.nb) np2 <<= 1;
-  // Rows of up to 1024 blocks: 256 threads and four rows per workgroup; longer rows: 1024 threads, one row
-  // (more rows per workgroup measured slower there: the register budget per thread halves).
+  // Rows of up to 1024 blocks: 256 threads, four blocks per thread and four rows per workgroup; longer rows
+  // (up to 4096 blocks): 512 threads, eight blocks per thread and two rows (1024 threads with one row, or two
+  // and four rows of 1024 threads, measured slower).
   if (np2 <= 1024) {
     const dim3 grid((unsigned)((g.Lq + 3) / 4), (unsigned)g.H);
     if (g.d == 128)
-      hipLaunchKernelGGL((select_kernel<128, 256, 4>), grid, dim3(256), 0, stream, q_pooled, k_pooled, g.Lq, g.nb, np2,
+      hipLaunchKernelGGL((select_kernel<128, 256, 4, 4>), grid, dim3(256), 0, stream, q_pooled, k_pooled, g.Lq, g.nb, np2,
                          scale, tau, k_min, mask, pitch);
     else
-      hipLaunchKernelGGL((select_kernel<64, 256, 4>), grid, dim3(256), 0, stream, q_pooled, k_pooled, g.Lq, g.nb, np2,
+      hipLaunchKernelGGL((select_kernel<64, 256, 4, 4>), grid, dim3(256), 0, stream, q_pooled, k_pooled, g.Lq, g.nb, np2,
                          scale, tau, k_min, mask, pitch);
   } else {
-    const dim3 grid((unsigned)g.Lq, (unsigned)g.H);
+    const dim3 grid((unsigned)((g.Lq + 1) / 2), (unsigned)g.H);
     if (g.d == 128)
-      hipLaunchKernelGGL((select_kernel<128, 1024, 1>), grid, dim3(1024), 0, stream, q_pooled, k_pooled, g.Lq, g.nb,
+      hipLaunchKernelGGL((select_kernel<128, 512, 2, 8>), grid, dim3(512), 0, stream, q_pooled, k_pooled, g.Lq, g.nb,
                          np2, scale, tau, k_min, mask, pitch);
     else
-      hipLaunchKernelGGL((select_kernel<64, 1024, 1>), grid, dim3(1024), 0, stream, q_pooled, k_pooled, g.Lq, g.nb,
+      hipLaunchKernelGGL((select_kernel<64, 512, 2, 8>), grid, dim3(512), 0, stream, q_pooled, k_pooled, g.Lq, g.nb,
                          np2, scale, tau, k_min, mask, pitch);
   }
   return hipGetLastError();
