@@ -6,7 +6,7 @@
 // 16-byte loads, fp32 sums, row groups combined through LDS in a fixed order).  HBM-bound: it reads
 // every token of K once.
 //
-// select_kernel: one workgroup per (head, R consecutive local query blocks); every thread keeps up to four
+// select_kernel: one workgroup per (head, R consecutive local query blocks); every thread keeps four or eight
 // of each row's blocks in registers, and the R rows share every pooled-key read and every reduction.  Block
 // scores s_j = scale <q, k_j> against every pooled key are keyed so that ascending key order is descending
 // score (equal scores: ascending block); the softmax weights exp(s - max) are summed, and the smallest key
