@@ -10,8 +10,9 @@ attention (sparsp_block_sparse_attn), all enqueued on torch's current stream.
 Prints one JSON line.  ``value`` is the effective attention throughput of the whole step: the
 algorithmic FLOPs of the selected tiles (4*b*b*d per selected (head, query block, key block)) divided by
 the step time.  Per-kernel durations come from HIP events recorded on the launch stream around every
-call in the timed steps.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the same
-workload.
+call in the timed steps.  After them, a few cold-cache repetitions time the pack and the attention with
+the L2s and the Infinity Cache flushed before each.  ``cpu_baseline`` times the fp64 CPU oracle on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -29,6 +30,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_DENSE_TFLOPS = 2500.0     # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "block-sparse attn effective TFLOP/s + KV pack GB/s, one rank's share"
+COLD_REPS = 5                  # cold-cache repetitions after the timed steps
+FLUSH_BYTES = 512 << 20        # read before a cold launch: twice the 256 MB Infinity Cache
 
 
 def parse():
@@ -40,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-comm", action="store_true", help="skip the communication-volume accounting")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle attention sample")
+    ap.add_argument("--cold-reps", type=int, default=COLD_REPS,
+                    help="repetitions with the caches flushed before the pack and before the attention")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="after the warmup, run one plain float32 device copy of this many MiB (read + write of "
                          "known size) so profiler byte counters can be scaled against it")
@@ -262,9 +267,48 @@ def main():
     wall = time.perf_counter() - t0
     ms = lambda a, b: float(np.mean([e[a].elapsed_time(e[b]) for e in events]))  # noqa: E731
     t_union, t_pack, t_attn = ms(0, 1), ms(1, 2), ms(2, 3)
+    warm_pack = [e[1].elapsed_time(e[2]) for e in events]
+    warm_attn = [e[2].elapsed_time(e[3]) for e in events]
     ms_per_step = wall * 1e3 / args.steps
     print(f"[bench] {w.name}: union {t_union * 1e3:.1f} us, pack {t_pack * 1e3:.1f} us, "
           f"attention {t_attn:.3f} ms, step {ms_per_step:.3f} ms", file=sys.stderr, flush=True)
+
+    # Cold caches: before the union + pack and again before the attention, a read of twice the Infinity
+    # Cache's size evicts the L2s and the Infinity Cache, so each timed kernel starts with its inputs in HBM.
+    # A read, not a write: a written flush buffer would leave dirty lines whose write-back the next kernel
+    # pays for (measured: 40 us, 8 %, on the hunyuan pack).
+    cold = None
+    if args.cold_reps > 0:
+        flush = torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device="cuda")
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.cold_reps)]
+        for e in cev:
+            flush.sum()
+            e[0].record(stream)
+            bsa.demand_union(g, mask, placement, out=u)
+            e[1].record(stream)
+            bsa.pack_kv(g, K, V, u, out=packed)
+            e[2].record(stream)
+            flush.sum()
+            e[3].record(stream)
+            bsa.block_sparse_attn(g, Q, mask, u.slot_of, packed, scale, out=(O, lse))
+            e[4].record(stream)
+        torch.cuda.synchronize()
+        del flush
+        c_union = [e[0].elapsed_time(e[1]) for e in cev]
+        c_pack = [e[1].elapsed_time(e[2]) for e in cev]
+        c_attn = [e[3].elapsed_time(e[4]) for e in cev]
+        cold = {
+            "reps": args.cold_reps,
+            "union_compact_us_median": round(float(np.median(c_union)) * 1e3, 2),
+            "pack_us_median": round(float(np.median(c_pack)) * 1e3, 2),
+            "pack_us_min": round(min(c_pack) * 1e3, 2),
+            "pack_GBps_median": round(pack_bytes / (float(np.median(c_pack)) * 1e-3) / 1e9, 1),
+            "attn_ms_median": round(float(np.median(c_attn)), 4),
+            "attn_ms_min": round(min(c_attn), 4),
+            "attn_TFLOPs_median": round(attn_flops / (float(np.median(c_attn)) * 1e-3) / 1e12, 2),
+        }
+        print(f"[bench] {w.name}: cold caches: pack {cold['pack_us_median']:.1f} us, attention "
+              f"{cold['attn_ms_median']:.3f} ms (medians of {args.cold_reps})", file=sys.stderr, flush=True)
 
     # Segment-wise consumption: attention over each source rank's segment (local first, then ring
     # distance 1, 2, ...) and the log-sum-exp merge of the partial results, as the payload would arrive.
@@ -418,6 +462,11 @@ def main():
             "attn_ms": round(t_attn, 4),
             "attn_TFLOPs": round(attn_tflops, 2),
             "attn_frac_bf16": round(attn_tflops / BF16_DENSE_TFLOPS, 4),
+            "warm": {"pack_us_median": round(float(np.median(warm_pack)) * 1e3, 2),
+                     "pack_us_min": round(min(warm_pack) * 1e3, 2),
+                     "attn_ms_median": round(float(np.median(warm_attn)), 4),
+                     "attn_ms_min": round(min(warm_attn), 4)},
+            "cold": cold,
             "segmented_attn_ms": round(seg_total, 4),
             "segmented_attn_TFLOPs": round(attn_flops / (seg_total * 1e-3) / 1e12, 2),
             "merge_us": round(merge_ms * 1e3, 2),

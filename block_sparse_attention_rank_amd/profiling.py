@@ -2,14 +2,15 @@
 
     python -m block_sparse_attention_rank_amd.profiling trace  KT_DIR  --warmup W --steps K
     python -m block_sparse_attention_rank_amd.profiling traffic FETCH_DIR WRITE_DIR --warmup W --steps K \
-        --workload NAME --calibration-mib MIB [--json-dir profiles]
+        --workload NAME --calibration-mib MIB [--cold-reps C] [--json-dir profiles]
     python -m block_sparse_attention_rank_amd.profiling attn-counters PMC_DIR --warmup W --steps K
 
 The inputs are the directories written by ``rocprofv3 --kernel-trace --stats --output-format csv -o run``
 and ``rocprofv3 --pmc <counter> --output-format csv -o run`` around ``bench.py``.  bench.py launches, in
-order: W + K single-pass steps (union, compaction, pack, attention), then the segment-wise attention and
-its merges, the permutation legs, a device copy and the mask materialisation legs; the first W + K
-launches of bsa_fwd_kernel and pack_kernel are the single-pass ones and the last K of them are timed.
+order: W + K single-pass steps (union, compaction, pack, attention), C cold-cache repetitions of the same
+launches (each after a fill that flushes the caches), then the segment-wise attention and its merges, the
+permutation legs and the mask materialisation legs; the first W + K launches of bsa_fwd_kernel and
+pack_kernel are the single-pass ones and the last K of them are timed.
 """
 from __future__ import annotations
 
@@ -91,15 +92,18 @@ def _calibration(disp, warmup: int):
     return cands[-1] if cands else None
 
 
-def _single_pass(disp, warmup: int, steps: int):
-    """Per kernel, the dispatches that one step of the path makes (warmup and timed steps), plus all
-    dispatches of the other kernels grouped by grid size."""
+def _single_pass(disp, warmup: int, steps: int, cold_reps: int = 0):
+    """Per kernel, the dispatches that one step of the path makes (warmup and timed steps), those of the
+    cold-cache repetitions, plus all dispatches of the other kernels grouped by grid size."""
     groups = defaultdict(list)
     seen = defaultdict(int)
     for d, k, grid, v, dur in disp:
         if k in ("bsa_fwd_kernel", "pack_kernel", "union_kernel", "compact_kernel"):
             seen[k] += 1
-            if seen[k] > warmup + steps:
+            if warmup + steps < seen[k] <= warmup + steps + cold_reps:
+                groups[(k + " (cold caches)", None)].append(v)
+                continue
+            if seen[k] > warmup + steps + cold_reps:
                 if k != "bsa_fwd_kernel":
                     continue
                 groups[(k + " (segments)", None)].append(v)
@@ -111,14 +115,14 @@ def _single_pass(disp, warmup: int, steps: int):
 
 
 def traffic(fetch_dir: str, write_dir: str, warmup: int, steps: int, workload: str, calib_mib: int,
-            json_dir: str | None, digests: dict | None) -> str:
+            json_dir: str | None, digests: dict | None, cold_reps: int = 0) -> str:
     f = _counter_by_dispatch(fetch_dir, "FETCH_SIZE")
     w = _counter_by_dispatch(write_dir, "WRITE_SIZE")
     calib_kib = calib_mib * 1024
     f_cal, w_cal = _calibration(f, warmup), _calibration(w, warmup)
     rs = calib_kib / f_cal if f_cal else 1.0
     ws = calib_kib / w_cal if w_cal else 1.0
-    gf, gw = _single_pass(f, warmup, steps), _single_pass(w, warmup, steps)
+    gf, gw = _single_pass(f, warmup, steps, cold_reps), _single_pass(w, warmup, steps, cold_reps)
     out = [f"Calibration: a float32 multiply of {calib_mib} MiB reads and writes exactly {calib_mib} MiB; FETCH_SIZE "
            f"reports {f_cal:.0f} KiB and WRITE_SIZE {w_cal:.0f} KiB for it, so the read scale is {rs:.4f} and the "
            f"write scale {ws:.4f}.", "",
@@ -194,6 +198,7 @@ def main():
     ap.add_argument("--steps", type=int, required=True)
     ap.add_argument("--workload", default="hunyuan")
     ap.add_argument("--calibration-mib", type=int, default=1024)
+    ap.add_argument("--cold-reps", type=int, default=0, help="bench.py's --cold-reps of the profiled run")
     ap.add_argument("--json-dir", default=None)
     a = ap.parse_args()
     if a.mode == "trace":
@@ -205,7 +210,8 @@ def main():
         bench = importlib.util.module_from_spec(spec)
         spec.loader.exec_module(bench)
         digests = {k: bench.kernel_sources_digest(k) for k in ("bsa_fwd", "pack")}
-        print(traffic(a.dirs[0], a.dirs[1], a.warmup, a.steps, a.workload, a.calibration_mib, a.json_dir, digests))
+        print(traffic(a.dirs[0], a.dirs[1], a.warmup, a.steps, a.workload, a.calibration_mib, a.json_dir, digests,
+                      a.cold_reps))
     else:
         print(attn_counters(a.dirs[0], a.warmup, a.steps))
 

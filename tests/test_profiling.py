@@ -56,3 +56,22 @@ def test_traffic_calibration_and_scaling(tmp_path):
     rec = json.load(open(tmp_path / "pack_unit_traffic.json"))
     assert rec["read_bytes"] == 100 * 1024 * 2 and rec["write_bytes"] == 300 * 1024
     assert rec["sources_digest"] == "abc"
+
+
+def test_traffic_cold_repetitions_kept_apart(tmp_path):
+    # warmup 1 + timed 1 single-pass packs, then 2 cold-cache packs with more HBM traffic: the single-pass
+    # record averages only the first two, the cold ones get their own row
+    seq = [("pack_kernel", 100.0), ("vectorized_elementwise_kernel", 512.0), ("union_kernel", 0),
+           ("pack_kernel", 100.0), ("pack_kernel", 400.0), ("pack_kernel", 600.0)]
+
+    def rows(counter):
+        return [{"Dispatch_Id": i + 1, "Kernel_Name": _name(k) if "elementwise" not in k else f"void {k}<4>(int)",
+                 "Grid_Size": 256, "Counter_Name": counter, "Counter_Value": v, "Start_Timestamp": 0,
+                 "End_Timestamp": 1000} for i, (k, v) in enumerate(seq)]
+    _write(str(tmp_path / "f" / "run_counter_collection.csv"), PMC_FIELDS, rows("FETCH_SIZE"))
+    _write(str(tmp_path / "w" / "run_counter_collection.csv"), PMC_FIELDS, rows("WRITE_SIZE"))
+    out = P.traffic(str(tmp_path / "f"), str(tmp_path / "w"), warmup=1, steps=1, workload="unit", calib_mib=1,
+                    json_dir=str(tmp_path), digests={}, cold_reps=2)
+    rec = json.load(open(tmp_path / "pack_unit_traffic.json"))
+    assert rec["read_bytes"] == 100 * 1024 * 2
+    assert "| pack_kernel (cold caches) | - | 2 | 500.0 |" in out
