@@ -116,6 +116,13 @@ def cpu_baseline(inp, budget_s: float, pairs: int, attn_flops: float):
             break
     t_attn_full = t_attn * pairs / max(done_pairs, 1)
     t_step = t_union + t_pack + t_attn_full
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:  # pragma: no cover
+        pass
+    slot_bytes = 2 * w.b * w.d * 2
     return {
         "value": attn_flops / t_step / 1e12,
         "unit": "TFLOP/s",
@@ -127,6 +134,13 @@ def cpu_baseline(inp, budget_s: float, pairs: int, attn_flops: float):
                    f"{t_attn_full:.0f} s; value = all tiles' FLOPs / ({t_union:.2f} + {t_pack:.2f} + "
                    f"{t_attn_full:.0f}) s"),
         "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model,
+        "union_compact_s": round(t_union, 4),
+        "union_mask_GBps": round(inp["mask"].size / t_union / 1e9, 3),
+        "pack_s": round(t_pack, 4),
+        "pack_GBps": round(2 * len(c["slot_block"]) * slot_bytes / t_pack / 1e9, 3),
+        "attn_sample_s": round(t_attn, 2),
+        "attn_GFLOPs": round(4.0 * w.b * w.b * w.d * done_pairs / t_attn / 1e9, 2),
     }
 
 
