@@ -179,23 +179,26 @@ __device__ __forceinline__ void unit_mask(f32x16& sacc, int lim) {
   }
 }
 
-// Probabilities of a unit, rounded to bf16 for the second product; the fp32 values are summed into
-// l_run (two add chains).  pf[b] holds keys 16b + 8 half + 0..7 of the unit.  (A v_dot2 against (1, 1)
-// would sum the rounded pairs in half the instructions, but on gfx950 it competes with the MFMAs of the
-// other wave on the SIMD and issues several times slower than two adds.)
-__device__ __forceinline__ void unit_probabilities(const f32x16& sacc, float scale_log2, float m_run, bf16x8 (&pf)[2],
-                                                   float& l_run) {
-  float l_odd = 0.f;
+// Probabilities of a unit, rounded to bf16 for the second product; returns the sum of their fp32 values
+// (two add chains, each seeded with its first term: p >= +0, so this equals a sum started from zero
+// without the two additions of zero the compiler would have to keep).  pf[b] holds keys 16b + 8 half +
+// 0..7 of the unit.  (A v_dot2 against (1, 1) would sum the rounded pairs in half the instructions, but
+// on gfx950 it competes with the MFMAs of the other wave on the SIMD and issues several times slower
+// than two adds.)
+__device__ __forceinline__ float unit_probabilities(const f32x16& sacc, float scale_log2, float m_run, bf16x8 (&pf)[2]) {
+  float p[16];
 #pragma unroll
   for (int x = 0; x < 16; ++x) {
-    const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[x], scale_log2, -m_run));
-    pf[x / 8][x % 8] = (__bf16)p;
-    if (x & 1)
-      l_odd += p;
-    else
-      l_run += p;
+    p[x] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[x], scale_log2, -m_run));
+    pf[x / 8][x % 8] = (__bf16)p[x];
   }
-  l_run += l_odd;
+  float l_even = p[0], l_odd = p[1];
+#pragma unroll
+  for (int x = 2; x < 16; x += 2) {
+    l_even += p[x];
+    l_odd += p[x + 1];
+  }
+  return l_even + l_odd;
 }
 
 // O^T += V^T P^T for unit g: step b covers keys 32g + 16b + 8 half + 0..7 of the stage, one V^T fragment.
@@ -232,15 +235,13 @@ __device__ __forceinline__ void unit_rescale(const f32x16& sacc, RowState<D, B>&
 #pragma unroll
     for (int i = 0; i < T::NDT; ++i) rs.oacc[i] *= alpha;
   }
-  lu = 0.f;
-  unit_probabilities(sacc, scale_log2, m_new == -INFINITY ? 0.f : m_new, pf, lu);
+  lu = unit_probabilities(sacc, scale_log2, m_new == -INFINITY ? 0.f : m_new, pf);
 }
 
 // Softmax of a unit whose P V product follows at once (the d = 128 schedule).
 template <int D, int B>
 __device__ __forceinline__ void unit_softmax(const f32x16& sacc, RowState<D, B>& rs, float scale_log2, bf16x8 (&pf)[2]) {
-  float lu = 0.f;
-  unit_probabilities(sacc, scale_log2, rs.m_run, pf, lu);
+  float lu = unit_probabilities(sacc, scale_log2, rs.m_run, pf);
   if (__builtin_amdgcn_ballot_w64(!(lu < 0x1p64f)) != 0) unit_rescale<D, B>(sacc, rs, scale_log2, pf, lu);
   rs.l_run += lu;
 }
@@ -362,10 +363,9 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         auto unit = [&](f32x16& cur, f32x16& nxt, const unsigned char* kbuf_next, int g_next,
                         const unsigned char* vbuf_prev, int g_prev, int lim) {
           bf16x8 pf[2];
-          float lu = 0.f;
           unit_mask(cur, lim);
           nxt = unit_scores<D, B>(kbuf_next, g_next, kread, qf);
-          unit_probabilities(cur, scale_log2, rs.m_run, pf, lu);
+          float lu = unit_probabilities(cur, scale_log2, rs.m_run, pf);
           unit_accumulate<D, B>(vbuf_prev, g_prev, vread, pfp, rs.oacc);
           if (__builtin_amdgcn_ballot_w64(!(lu < 0x1p64f)) != 0) unit_rescale<D, B>(cur, rs, scale_log2, pf, lu);
           rs.l_run += lu;
