@@ -114,6 +114,30 @@ def test_argument_checks():
     assert b"slot_capacity" in lib.sparsp_last_error()
 
 
+def test_segment_and_merge_argument_checks():
+    lib = bsa.load()
+    g = _geom()
+    gp = ctypes.byref(g)
+    E, U = _lib.SPARSP_ERR_INVALID, _lib.SPARSP_ERR_UNSUPPORTED
+    for fn in (lib.sparsp_block_sparse_attn_segment, lib.sparsp_block_sparse_attn_segment_accumulate):
+        assert fn(gp, FAKE, FAKE, 64, FAKE, FAKE, -1, 4, 0.1, FAKE, FAKE, None) == E          # slot_lo < 0
+        assert b"slot_lo" in lib.sparsp_last_error()
+        assert fn(gp, FAKE, FAKE, 64, FAKE, FAKE, 5, 4, 0.1, FAKE, FAKE, None) == E           # hi < lo
+        assert fn(gp, None, FAKE, 64, FAKE, FAKE, 0, 4, 0.1, FAKE, FAKE, None) == E
+        assert fn(gp, FAKE, FAKE, 64, FAKE, FAKE, 0, 4, float("inf"), FAKE, FAKE, None) == E
+        assert fn(gp, FAKE, FAKE, 64, FAKE, FAKE, 0, 4, 0.1, FAKE + 4, FAKE, None) == E       # O misaligned
+        assert fn(gp, FAKE, FAKE, 8, FAKE, FAKE, 0, 4, 0.1, FAKE, FAKE, None) == E            # pitch < nb
+        assert fn(ctypes.byref(_geom(d=96)), FAKE, FAKE, 64, FAKE, FAKE, 0, 4, 0.1, FAKE, FAKE, None) == U
+        assert fn(None, FAKE, FAKE, 64, FAKE, FAKE, 0, 4, 0.1, FAKE, FAKE, None) == E
+    mp = lib.sparsp_merge_partial
+    assert mp(None, FAKE, FAKE, FAKE, FAKE, None) == E
+    assert mp(gp, None, FAKE, FAKE, FAKE, None) == E
+    assert mp(gp, FAKE, FAKE, FAKE, None, None) == E
+    assert mp(gp, FAKE, FAKE, FAKE + 8, FAKE, None) == E                                       # O_part misaligned
+    assert b"aligned" in lib.sparsp_last_error()
+    assert mp(ctypes.byref(_geom(b=32)), FAKE, FAKE, FAKE, FAKE, None) == U
+
+
 def test_compaction_lds_limit():
     """A geometry whose compaction tables exceed 64 KiB of LDS is refused, not launched."""
     lib = bsa.load()
