@@ -84,7 +84,7 @@ __device__ __forceinline__ void copy16(const char* base, uint32_t voff, const un
 
 constexpr int kStageKeys = 64;     // keys per pipeline stage
 constexpr int kXcdChunk = 16;      // consecutive (head, query block) items kept on one XCD
-constexpr int kListCap = 512;      // selected blocks listed per pass over the mask row
+constexpr int kListCols = 4;       // mask columns a thread reads per listing step (one 32-bit load)
 
 template <int D, int B>
 struct Tile {
@@ -100,6 +100,9 @@ struct Tile {
   static constexpr int NDT = D / 32;                     // 32-row tiles of O^T
   static constexpr int NQF = D / 16;                     // Q fragments along d
   static constexpr int64_t SLOT_BYTES = 4ll * B * D;     // bytes per packed slot
+  // Selected blocks listed per pass over the mask row: room for two listing steps, except at d = 64,
+  // b = 128, where one step's worth keeps four workgroups within a CU's 160 KiB of LDS.
+  static constexpr int LIST = (D == 64 && B == 128) ? kListCols * NT : 2 * kListCols * NT;
   static_assert(CH % NT == 0, "stage must split evenly over the threads");
   static_assert(NT * 16 == 64 * 16 * NW, "one 1 KiB LDS span per wave and copy");
   static_assert(2 * STAGE <= 65536, "LDS offsets must fit the 16-bit immediate");
@@ -272,7 +275,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   __shared__ __align__(1024) unsigned char sK1[T::KBYTES];
   __shared__ __align__(1024) unsigned char sV0[D * T::VROW];
   __shared__ __align__(1024) unsigned char sV1[D * T::VROW];
-  __shared__ int sList[kListCap];
+  __shared__ int sList[T::LIST];
   __shared__ int sWaveCnt[T::NW];
 
   const int wid = xcd_chunked<kXcdChunk>(blockIdx.x);
@@ -319,28 +322,50 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   int col = 0;
   int seen = 0;  // selected blocks in the slot range, over all passes
   while (col < nb) {
-    // List the selected blocks of the next columns (ascending j) as (slot << 1 | is_last_block).
+    // List the selected blocks of the next columns (ascending j) as (slot << 1 | is_last_block).  A thread
+    // reads kListCols consecutive mask bytes with one load (rows are 16-byte aligned and their pitch is a
+    // multiple of 16, so the word stays inside the row; columns >= nb are ignored) and looks up their slots;
+    // its entries go after those of the lower lanes and waves, whose counts come from one ballot per bit of
+    // the per-thread count.
     int total = 0;
-    while (col < nb && total <= kListCap - T::NT) {
-      const int j = col + t;
-      int slot = -1;
-      if (j < nb && mrow[j] != 0) {
-        slot = sof[j];
-        if (slot < slot_lo || slot >= slot_hi) slot = -1;  // outside the consumed slot range
+    while (col < nb && total <= T::LIST - kListCols * T::NT) {
+      const int j0 = col + kListCols * t;
+      const uint32_t mbits = j0 < nb ? *reinterpret_cast<const uint32_t*>(mrow + j0) : 0u;
+      int slots[kListCols];
+      int cnt = 0;
+#pragma unroll
+      for (int c = 0; c < kListCols; ++c) {
+        const int j = j0 + c;
+        int slot = -1;
+        if (j < nb && ((mbits >> (8 * c)) & 0xffu) != 0u) {
+          slot = sof[j];
+          if (slot < slot_lo || slot >= slot_hi) slot = -1;  // outside the consumed slot range
+        }
+        slots[c] = slot;
+        cnt += slot >= 0 ? 1 : 0;
       }
-      const uint64_t bal = __builtin_amdgcn_ballot_w64(slot >= 0);
-      if (lane == 0) sWaveCnt[wave] = __popcll(bal);
+      int below = 0, wave_total = 0;  // entries of the lower lanes of this wave; of the whole wave
+#pragma unroll
+      for (int bit = 0; bit < 3; ++bit) {  // cnt <= 4 < 8
+        const uint64_t bal = __builtin_amdgcn_ballot_w64((cnt >> bit) & 1);
+        below += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))
+                 << bit;
+        wave_total += __popcll(bal) << bit;
+      }
+      if (lane == 0) sWaveCnt[wave] = wave_total;
       __syncthreads();
-      int off = total, add = 0;
+      int off = total + below, add = 0;
 #pragma unroll
       for (int w = 0; w < T::NW; ++w) {
         const int c = sWaveCnt[w];
         off += w < wave ? c : 0;
         add += c;
       }
-      if (slot >= 0) sList[off + __popcll(bal & ((1ull << lane) - 1ull))] = (slot << 1) | (j == nb - 1 ? 1 : 0);
+#pragma unroll
+      for (int c = 0; c < kListCols; ++c)
+        if (slots[c] >= 0) sList[off++] = (slots[c] << 1) | (j0 + c == nb - 1 ? 1 : 0);
       total += add;
-      col += T::NT;
+      col += kListCols * T::NT;
       __syncthreads();
     }
 
