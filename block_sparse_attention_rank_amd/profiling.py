@@ -1,6 +1,7 @@
 """Summaries of rocprofv3 CSV output for the library's kernels (measurement tooling; no GPU needed).
 
     python -m block_sparse_attention_rank_amd.profiling trace  KT_DIR  --warmup W --steps K
+    python -m block_sparse_attention_rank_amd.profiling stats  KT_DIR  --warmup W --steps K
     python -m block_sparse_attention_rank_amd.profiling traffic FETCH_DIR WRITE_DIR --warmup W --steps K \
         --workload NAME --calibration-mib MIB [--cold-reps C] [--json-dir profiles]
     python -m block_sparse_attention_rank_amd.profiling attn-counters PMC_DIR --warmup W --steps K
@@ -66,6 +67,17 @@ def trace(kt_dir: str, warmup: int, steps: int) -> str:
         if v:
             med = sorted(v)[len(v) // 2]
             out.append(f"| {k} | {len(v)} | {sum(v) / len(v):.1f} | {med:.1f} |")
+    return "\n".join(out)
+
+
+def stats(kt_dir: str) -> str:
+    """rocprofv3's own --stats table (every launch of each kernel), with short kernel names."""
+    rows = _rows(_find(kt_dir, "kernel_stats.csv"))
+    out = ["| kernel | calls | total ms | average us | min us | max us | share |", "|---|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        out.append(f"| {short_name(r['Name'])} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.2f} | "
+                   f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                   f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} % |")
     return "\n".join(out)
 
 
@@ -192,7 +204,7 @@ def attn_counters(pmc_dir: str, warmup: int, steps: int) -> str:
 
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("mode", choices=["trace", "traffic", "attn-counters"])
+    ap.add_argument("mode", choices=["trace", "stats", "traffic", "attn-counters"])
     ap.add_argument("dirs", nargs="+")
     ap.add_argument("--warmup", type=int, required=True)
     ap.add_argument("--steps", type=int, required=True)
@@ -203,6 +215,8 @@ def main():
     a = ap.parse_args()
     if a.mode == "trace":
         print(trace(a.dirs[0], a.warmup, a.steps))
+    elif a.mode == "stats":
+        print(stats(a.dirs[0]))
     elif a.mode == "traffic":
         import importlib.util
         root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

@@ -75,3 +75,15 @@ def test_traffic_cold_repetitions_kept_apart(tmp_path):
     rec = json.load(open(tmp_path / "pack_unit_traffic.json"))
     assert rec["read_bytes"] == 100 * 1024 * 2
     assert "| pack_kernel (cold caches) | - | 2 | 500.0 |" in out
+
+
+def test_stats_table(tmp_path):
+    fields = ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"]
+    _write(str(tmp_path / "kt" / "run_kernel_stats.csv"), fields, [
+        {"Name": _name("pack_kernel"), "Calls": 2, "TotalDurationNs": 1000000, "AverageNs": 500000, "Percentage": 20.0,
+         "MinNs": 400000, "MaxNs": 600000, "StdDev": 1},
+        {"Name": _name("bsa_fwd_kernel"), "Calls": 2, "TotalDurationNs": 4000000, "AverageNs": 2000000,
+         "Percentage": 80.0, "MinNs": 1900000, "MaxNs": 2100000, "StdDev": 1}])
+    out = P.stats(str(tmp_path / "kt")).splitlines()
+    assert out[2] == "| bsa_fwd_kernel | 2 | 4.00 | 2000.0 | 1900.0 | 2100.0 | 80.0 % |"
+    assert out[3].startswith("| pack_kernel | 2 | 1.00 | 500.0 |")
