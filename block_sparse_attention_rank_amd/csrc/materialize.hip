@@ -130,24 +130,72 @@ __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qp
   const float4* kh = reinterpret_cast<const float4*>(kp + (int64_t)h * nb * D);
   uint64_t key[R][PER];
   float w[R][PER];
+  if constexpr (D == 64) {
+    // d = 64: the dot products are split over quads of lanes: lane i of a quad holds elements [16 i, 16 i + 16)
+    // of each row's pooled query in registers and computes that slice of the dot products of the blocks owned
+    // by the quad's four threads (the quad reads each pooled-key row as one contiguous 256-byte span); the
+    // slices are summed across the quad in a fixed order with DPP.  (At d = 128 the same split over eight
+    // lanes measured slower than whole dot products per thread.)
+    const int gi = lane % 4;
+    float qs[R][16];
 #pragma unroll
-  for (int r = 0; r < PER; ++r) {
-    const int j = t + r * NT;
+    for (int q = 0; q < R; ++q)
 #pragma unroll
-    for (int q = 0; q < R; ++q) key[q][r] = ~0ull;
-    if (j < nb) {
-      float s[R];
+      for (int e = 0; e < 16; ++e) qs[q][e] = qv[q][gi * 16 + e];
 #pragma unroll
-      for (int q = 0; q < R; ++q) s[q] = 0.f;
-#pragma unroll 4
-      for (int c = 0; c < D / 4; ++c) {
-        const float4 kv = kh[(int64_t)j * (D / 4) + c];
+    for (int r = 0; r < PER; ++r) {
+      float sc[R];
 #pragma unroll
-        for (int q = 0; q < R; ++q)
-          s[q] += qv[q][4 * c] * kv.x + qv[q][4 * c + 1] * kv.y + qv[q][4 * c + 2] * kv.z + qv[q][4 * c + 3] * kv.w;
+      for (int q = 0; q < R; ++q) sc[q] = 0.f;
+#pragma unroll
+      for (int o = 0; o < 4; ++o) {
+        const int j = (t - gi + o) + r * NT;  // block of the quad's o-th thread (the same for the whole quad)
+        float part[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q) part[q] = 0.f;
+        if (j < nb) {
+          const float4* kr = kh + (int64_t)j * (D / 4) + gi * 4;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float4 kv = kr[c];
+#pragma unroll
+            for (int q = 0; q < R; ++q)
+              part[q] += qs[q][4 * c] * kv.x + qs[q][4 * c + 1] * kv.y + qs[q][4 * c + 2] * kv.z + qs[q][4 * c + 3] * kv.w;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < R; ++q) {
+          float v = part[q];
+          v += __int_as_float(dpp_step<0xB1, 0xF>(__float_as_int(v)));  // quad_perm [1, 0, 3, 2]
+          v += __int_as_float(dpp_step<0x4E, 0xF>(__float_as_int(v)));  // quad_perm [2, 3, 0, 1]
+          if (gi == o) sc[q] = v;
+        }
       }
+      const int j = t + r * NT;
 #pragma unroll
-      for (int q = 0; q < R; ++q) key[q][r] = ((uint64_t)(~ordered_bits(s[q] * scale)) << 32) | (uint32_t)j;
+      for (int q = 0; q < R; ++q)
+        key[q][r] = j < nb ? ((uint64_t)(~ordered_bits(sc[q] * scale)) << 32) | (uint32_t)j : ~0ull;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+      const int j = t + r * NT;
+#pragma unroll
+      for (int q = 0; q < R; ++q) key[q][r] = ~0ull;
+      if (j < nb) {
+        float s[R];
+#pragma unroll
+        for (int q = 0; q < R; ++q) s[q] = 0.f;
+#pragma unroll 4
+        for (int c = 0; c < D / 4; ++c) {
+          const float4 kv = kh[(int64_t)j * (D / 4) + c];
+#pragma unroll
+          for (int q = 0; q < R; ++q)
+            s[q] += qv[q][4 * c] * kv.x + qv[q][4 * c + 1] * kv.y + qv[q][4 * c + 2] * kv.z + qv[q][4 * c + 3] * kv.w;
+        }
+#pragma unroll
+        for (int q = 0; q < R; ++q) key[q][r] = ((uint64_t)(~ordered_bits(s[q] * scale)) << 32) | (uint32_t)j;
+      }
     }
   }
 
