@@ -8,6 +8,15 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+try:  # property tests draw the same examples on every run, so the suite's outcome is reproducible
+    from hypothesis import settings as _hyp_settings
+
+    _hyp_settings.register_profile("reproducible", derandomize=True)
+    _hyp_settings.load_profile("reproducible")
+except ImportError:  # pragma: no cover
+    pass
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")

@@ -109,7 +109,7 @@ CASES = {
     "d64_b128_ragged": (custom(H=2, d=64, T=3, HW=1000, b=128, G=3), 0.95, 1),
     "floor_everything": (custom(H=2, d=64, T=2, HW=700, b=64, G=2), 0.1, 10_000),
     "tau_one": (custom(H=2, d=128, T=2, HW=700, b=64, G=2), 1.0, 0),
-    # rows of more than 1024 blocks take the 1024-thread select
+    # rows of more than 1024 blocks take the 512-thread, two-row select
     "wide_d64": (custom(H=2, d=64, T=12, HW=6144, b=64, G=8, k_offset_sigma=3.0), 0.9, 16),
     "wide_d128_ragged": (custom(H=1, d=128, T=37, HW=3600, b=128, G=8), 0.5, 4),
 }
@@ -120,6 +120,39 @@ def test_mask_matches_oracle(require_gpu, case):
     w, tau, k_min = CASES[case]
     inp, g, qp, kp, mask = _run(w, tau, k_min)
     w = inp["workload"]
+    qo = O.pool_blocks(inp["Q"], w.b, w.N, inp["q_blocks"])
+    ko = O.pool_blocks(inp["K"], w.b, w.N)
+    aq = _abs_pool(inp["Q"], w.b, w.N, inp["q_blocks"])
+    ak = _abs_pool(inp["K"], w.b, w.N)
+    rows, exact = _check_rows(mask, qo, ko, aq, ak, 1 / math.sqrt(w.d), tau, k_min, w.b, w.d, w.nb)
+    assert exact >= 0.98 * rows, (exact, rows)
+
+
+def _random_case(i: int):
+    rng = np.random.default_rng([77, i])
+    d, b = int(rng.choice([64, 128])), int(rng.choice([64, 128]))
+    if i % 2:  # rows of 1024 to about 4000 blocks: the long-row select
+        T, HW, G = int(rng.integers(16, 32)), int(rng.integers(64 * b, 124 * b)), int(rng.choice([4, 8]))
+    else:
+        T, HW, G = int(rng.integers(1, 6)), int(rng.integers(b, 40 * b)), int(rng.choice([1, 2, 4, 8]))
+    w = custom(name=f"mat_random{i}", H=int(rng.integers(1, 3)), d=d, b=b, T=T, HW=HW, G=G, r=int(rng.integers(G)),
+               k_offset_sigma=float(rng.choice([0.0, 3.0, 10.0])), seed=500 + i)
+    return w, float(rng.choice([0.0, 0.5, 0.85, 0.9, 0.99, 1.0])), int(rng.integers(0, 40))
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_geometries(require_gpu, i):
+    """Seeded random geometries (both head dims and block sizes, rows on both sides of 1024 blocks, random
+    tau and k_min) under the same validity rules."""
+    w, tau, k_min = _random_case(i)
+    if w.nb > 4096:
+        pytest.skip("rows of more than 4096 blocks are refused by the select")
+    inp, g, qp, kp, mask = _run(w, tau, k_min)
+    w = inp["workload"]
+    if len(inp["q_blocks"]) == 0:
+        return
+    print(f"[materialize] random {i}: H={w.H} d={w.d} b={w.b} nb={w.nb} Lq={len(inp['q_blocks'])} tau={tau} "
+          f"k_min={k_min}", flush=True)
     qo = O.pool_blocks(inp["Q"], w.b, w.N, inp["q_blocks"])
     ko = O.pool_blocks(inp["K"], w.b, w.N)
     aq = _abs_pool(inp["Q"], w.b, w.N, inp["q_blocks"])
@@ -164,8 +197,8 @@ def test_materialized_mask_feeds_the_path(require_gpu):
 
 
 def test_repeat_runs_are_bit_identical(require_gpu):
-    """Pooling sums in a fixed order and the select sorts and scans in a fixed order: two runs give the
-    same pooled tiles and the same mask, bit for bit (also at 1024 threads per row)."""
+    """Pooling sums in a fixed order and the select's threshold search reduces in a fixed order: two runs
+    give the same pooled tiles and the same mask, bit for bit (also on rows of more than 1024 blocks)."""
     for w in (CONFIGS["small"], custom(H=2, d=64, T=12, HW=6144, b=64, G=8)):
         a = _run(w, 0.9, 4)
         b = _run(w, 0.9, 4, inp=a[0])
