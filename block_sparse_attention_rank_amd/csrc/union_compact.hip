@@ -70,7 +70,7 @@ __global__ __launch_bounds__(kUnionThreads) void union_kernel(const uint8_t* __r
 // counts in (p, h') row-major order; workgroup 0 publishes that scan as seg_offsets.  It then numbers its
 // own head's demanded blocks: the slot of block j owned by p is the segment start of (p, h), plus the
 // demanded blocks of p in earlier words, plus those below j in the same word.
-constexpr int kCompactThreads = 256;
+constexpr int kCompactThreads = 1024;  // 16 waves: owner bitsets and slot numbering over more words at once
 
 __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
     const int32_t* __restrict__ placement, const uint64_t* __restrict__ demand, int H, int G, int nb, int W,
