@@ -281,6 +281,72 @@ def lse_merge(O_a, lse_a, O_b, lse_b):
 
 
 # --------------------------------------------------------------------------------------------------
+# the consumption schedule (section 7: the local block stays whole, remote blocks are cut into chunks, finer
+# for the final remote block where the pipeline drains (7.1, Figure 11); attention is partitioned by heads and
+# the chunk with the highest sparsity is scheduled last (7.2))
+
+
+def segment_tiles(mask: np.ndarray, placement: np.ndarray, G: int, nb: int) -> np.ndarray:
+    """tiles[p][h] = number of selected (local row k, key block j) pairs of head h with j owned by rank p: the
+    attention work (and the payload use) of head h's part of source rank p's segment.  Counted one by one."""
+    H, Lq = mask.shape[0], mask.shape[1]
+    P = [int(x) for x in np.asarray(placement).tolist()]
+    tiles = np.zeros((G, H), dtype=np.int64)
+    for h in range(H):
+        for k in range(Lq):
+            for j in np.flatnonzero(np.asarray(mask[h, k, :nb])):
+                tiles[P[int(j)], h] += 1
+    return tiles
+
+
+def chunk_plan(seg_offsets: np.ndarray, tiles: np.ndarray, G: int, H: int, r: int, chunks_steady: int,
+               chunks_drain: int) -> list[dict]:
+    """The order in which rank r consumes its payload, as a list of chunks {p, h_lo, h_hi, slot_lo, slot_hi,
+    tiles}.  Segments arrive in ring order p = r, r+1, ..., r+G-1 (mod G).  The local segment (p = r) is one
+    chunk.  Each remote segment is cut by heads into chunks_steady chunks, the last one to arrive into
+    chunks_drain chunks; c chunks over H heads (c at most H) are the head ranges [i*H//c, (i+1)*H//c).  A chunk
+    holds the slots of its heads in segment p (each head of a segment is contiguous).  Within a segment the
+    chunks run from the most selected tiles to the fewest (equal counts: lower heads first), so that the chunk
+    with the highest sparsity is the last.  Chunks without slots carry no payload and no work and are left
+    out."""
+    seg = [int(x) for x in np.asarray(seg_offsets).tolist()]
+    plan = []
+    for k in range(G):
+        p = (r + k) % G
+        if k == 0:
+            c = 1
+        elif k == G - 1:
+            c = chunks_drain
+        else:
+            c = chunks_steady
+        c = min(c, H)
+        chunks = []
+        for i in range(c):
+            h_lo, h_hi = i * H // c, (i + 1) * H // c
+            lo, hi = seg[p * H + h_lo], seg[p * H + h_hi]
+            if hi > lo:
+                chunks.append(dict(p=p, h_lo=h_lo, h_hi=h_hi, slot_lo=lo, slot_hi=hi,
+                                   tiles=int(sum(int(tiles[p, h]) for h in range(h_lo, h_hi)))))
+        chunks.sort(key=lambda ch: (-ch["tiles"], ch["h_lo"]))
+        plan.extend(chunks)
+    return plan
+
+
+def attention_block_slots(Q, K, V, mask, slot_of, slot_lo: int, slot_hi: int, h: int, k: int, b: int, N: int,
+                          scale: float):
+    """O and lse of local query block k of head h over the keys of the selected blocks whose packed slot lies
+    in [slot_lo, slot_hi): the definition of attention restricted to that key set ((0, -inf) if empty)."""
+    nb = -(-N // b)
+    row = np.array(mask[h, k, :nb], copy=True)
+    s = np.asarray(slot_of)[h, :nb]
+    row[(s < slot_lo) | (s >= slot_hi)] = 0
+    toks = allowed_keys(row, nb, b, N)
+    q = bf16_to_f64(Q[h, k * b:(k + 1) * b])
+    O, lse, _ = _attend(q, bf16_to_f64(K[h, toks]), bf16_to_f64(V[h, toks]), scale)
+    return O, lse
+
+
+# --------------------------------------------------------------------------------------------------
 # placement permutation (section 4.3: the placement is realised as a fixed permutation of logical blocks
 # to (rank, offset) pairs, applied to the hidden states before the distributed region and undone after it)
 
