@@ -14,11 +14,11 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from ._lib import EXPORTS, LIB_PATH, Geometry, SparspError, check, load  # noqa: F401
+from ._lib import EXPORTS, LIB_PATH, Chunk, Geometry, SparspError, check, load  # noqa: F401
 
 __all__ = ["Geometry", "SparspError", "UnionResult", "geometry", "local_query_blocks", "demand_union",
            "pack_kv", "block_sparse_attn", "block_sparse_attn_segment", "block_sparse_attn_segment_accumulate",
-           "merge_partial", "segment_ranges",
+           "merge_partial", "segment_ranges", "chunk_plan", "block_sparse_attn_chunk_accumulate", "Chunk",
            "placement_permutation", "permute_blocks", "demand_counts", "comm_volume", "pool_blocks",
            "materialize_mask", "load", "LIB_PATH", "EXPORTS"]
 
@@ -38,17 +38,59 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def _require(t, name, dtype, shape=None):
+    """Type, dtype, shape and layout of a tensor argument.  Every call checks all of its tensors this way
+    first and their device (_on_device) last, then calls the library."""
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _on_device(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+
+
+def _require_mask(mask, g: Geometry, name="mask"):
+    """The rank's mask rows: uint8 [H][Lq][pitch] with pitch >= nb and a multiple of 16."""
+    import torch
+    if not isinstance(mask, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if mask.dim() != 3 or mask.shape[0] != g.H or mask.shape[1] != g.Lq:
+        raise ValueError(f"{name} must be [H={g.H}][Lq={g.Lq}][pitch], got {tuple(mask.shape)}")
+    pitch = mask.shape[2]
+    if pitch < g.nb or pitch % 16:
+        raise ValueError(f"{name} pitch must be >= nb = {g.nb} and a multiple of 16, got {pitch}")
+    _require(mask, name, torch.uint8, (g.H, g.Lq, pitch))
+
+
+def _require_packed(packed, g: Geometry, min_slots: int = 1, name="packed"):
+    """The compacted buffer: bf16 [slots][2][b*d] with at least `min_slots` slots."""
+    import torch
+    if not isinstance(packed, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if packed.dim() != 3 or packed.shape[1] != 2 or packed.shape[2] != g.b * g.d:
+        raise ValueError(f"{name} must be [slots][2][b*d = {g.b * g.d}], got {tuple(packed.shape)}")
+    if packed.shape[0] < max(1, min_slots):
+        raise ValueError(f"{name} holds {packed.shape[0]} slots, needs at least {max(1, min_slots)}")
+    _require(packed, name, torch.bfloat16, tuple(packed.shape))
+
+
+def _require_outputs(out, g: Geometry):
+    """(O, lse): float32 [H][Lq*b][d] and [H][Lq*b]."""
+    import torch
+    if not isinstance(out, (tuple, list)) or len(out) != 2:
+        raise TypeError("out must be a pair (O, lse)")
+    O, lse = out
+    _require(O, "O", torch.float32, (g.H, g.Lq * g.b, g.d))
+    _require(lse, "lse", torch.float32, (g.H, g.Lq * g.b))
+    return O, lse
 
 
 def local_query_blocks(placement: np.ndarray, G: int, r: int) -> np.ndarray:
@@ -86,11 +128,18 @@ def empty_union(g: Geometry, device="cuda") -> UnionResult:
 def demand_union(g: Geometry, mask, placement, out: UnionResult | None = None, stream=None) -> UnionResult:
     """Per-head demand union and per-peer compaction (sparsp_demand_union)."""
     import torch
-    _require(mask, "mask", torch.uint8)
+    _require_mask(mask, g)
     _require(placement, "placement", torch.int32, (g.nb,))
-    if mask.dim() != 3 or mask.shape[0] != g.H or mask.shape[1] != g.Lq:
-        raise ValueError("mask must be [H][Lq][pitch]")
-    out = out or empty_union(g, mask.device)
+    if out is None:
+        out = empty_union(g, mask.device)
+    else:
+        _require(out.demand, "demand", torch.int64, (g.H, g.W))
+        _require(out.seg_offsets, "seg_offsets", torch.int32, (g.G * g.H + 1,))
+        _require(out.slot_block, "slot_block", torch.int32, (g.H * g.nb,))
+        _require(out.slot_head, "slot_head", torch.int32, (g.H * g.nb,))
+        _require(out.slot_of, "slot_of", torch.int32, (g.H, g.nb))
+    _on_device(mask=mask, placement=placement, demand=out.demand, seg_offsets=out.seg_offsets,
+               slot_block=out.slot_block, slot_head=out.slot_head, slot_of=out.slot_of)
     check(load().sparsp_demand_union(ctypes.byref(g), _ptr(mask), mask.shape[2], _ptr(placement), _ptr(out.demand),
                                      _ptr(out.seg_offsets), _ptr(out.slot_block), _ptr(out.slot_head),
                                      _ptr(out.slot_of), _stream(stream)))
@@ -105,12 +154,18 @@ def pack_kv(g: Geometry, K, V, u: UnionResult, slot_capacity: int | None = None,
     shape = (g.H, g.nb * g.b, g.d)
     _require(K, "K", torch.bfloat16, shape)
     _require(V, "V", torch.bfloat16, shape)
+    _require(u.seg_offsets, "seg_offsets", torch.int32, (g.G * g.H + 1,))
+    _require(u.slot_block, "slot_block", torch.int32, (g.H * g.nb,))
+    _require(u.slot_head, "slot_head", torch.int32, (g.H * g.nb,))
     cap = slot_capacity if slot_capacity is not None else g.H * g.nb
     if out is None:
+        if cap < 1:
+            raise ValueError("slot_capacity must be >= 1")
         out = torch.empty((cap, 2, g.b * g.d), dtype=torch.bfloat16, device=K.device)
     else:
-        _require(out, "packed", torch.bfloat16)
+        _require_packed(out, g)
         cap = out.shape[0]
+    _on_device(K=K, V=V, seg_offsets=u.seg_offsets, slot_block=u.slot_block, slot_head=u.slot_head, packed=out)
     check(load().sparsp_pack_kv(ctypes.byref(g), _ptr(K), _ptr(V), _ptr(u.seg_offsets), _ptr(u.slot_block),
                                 _ptr(u.slot_head), cap, _ptr(out), _stream(stream)))
     return out
@@ -123,15 +178,16 @@ def block_sparse_attn(g: Geometry, Q, mask, slot_of, packed, softmax_scale: floa
     Returns (O float32 [H][Lq*b][d], lse float32 [H][Lq*b])."""
     import torch
     _require(Q, "Q", torch.bfloat16, (g.H, g.Lq * g.b, g.d))
-    _require(mask, "mask", torch.uint8)
+    _require_mask(mask, g)
     _require(slot_of, "slot_of", torch.int32, (g.H, g.nb))
-    _require(packed, "packed", torch.bfloat16)
+    _require_packed(packed, g)
     scale = 1.0 / math.sqrt(g.d) if softmax_scale is None else float(softmax_scale)
     if out is None:
         O = torch.empty((g.H, g.Lq * g.b, g.d), dtype=torch.float32, device=Q.device)
         lse = torch.empty((g.H, g.Lq * g.b), dtype=torch.float32, device=Q.device)
     else:
-        O, lse = out
+        O, lse = _require_outputs(out, g)
+    _on_device(Q=Q, mask=mask, slot_of=slot_of, packed=packed, O=O, lse=lse)
     check(load().sparsp_block_sparse_attn(ctypes.byref(g), _ptr(Q), _ptr(mask), mask.shape[2], _ptr(slot_of),
                                           _ptr(packed), packed.shape[0], scale, _ptr(O), _ptr(lse),
                                           _stream(stream)))
@@ -143,7 +199,7 @@ def _attn_outputs(g: Geometry, Q, out):
     if out is None:
         return (torch.empty((g.H, g.Lq * g.b, g.d), dtype=torch.float32, device=Q.device),
                 torch.empty((g.H, g.Lq * g.b), dtype=torch.float32, device=Q.device))
-    return out
+    return _require_outputs(out, g)
 
 
 def block_sparse_attn_segment(g: Geometry, Q, mask, slot_of, packed, slot_lo: int, slot_hi: int,
@@ -152,13 +208,12 @@ def block_sparse_attn_segment(g: Geometry, Q, mask, slot_of, packed, slot_lo: in
     (sparsp_block_sparse_attn_segment).  Returns the partial (O, lse)."""
     import torch
     _require(Q, "Q", torch.bfloat16, (g.H, g.Lq * g.b, g.d))
-    _require(mask, "mask", torch.uint8)
+    _require_mask(mask, g)
     _require(slot_of, "slot_of", torch.int32, (g.H, g.nb))
-    _require(packed, "packed", torch.bfloat16)
-    if slot_hi > packed.shape[0]:
-        raise ValueError("packed holds fewer than slot_hi slots")
+    _require_packed(packed, g, min_slots=slot_hi)
     scale = 1.0 / math.sqrt(g.d) if softmax_scale is None else float(softmax_scale)
     O, lse = _attn_outputs(g, Q, out)
+    _on_device(Q=Q, mask=mask, slot_of=slot_of, packed=packed, O=O, lse=lse)
     check(load().sparsp_block_sparse_attn_segment(ctypes.byref(g), _ptr(Q), _ptr(mask), mask.shape[2],
                                                   _ptr(slot_of), _ptr(packed), int(slot_lo), int(slot_hi), scale,
                                                   _ptr(O), _ptr(lse), _stream(stream)))
@@ -171,17 +226,57 @@ def block_sparse_attn_segment_accumulate(g: Geometry, Q, mask, slot_of, packed, 
     (O, lse) in place (sparsp_block_sparse_attn_segment_accumulate); start from (0, -inf)."""
     import torch
     _require(Q, "Q", torch.bfloat16, (g.H, g.Lq * g.b, g.d))
-    _require(mask, "mask", torch.uint8)
+    _require_mask(mask, g)
     _require(slot_of, "slot_of", torch.int32, (g.H, g.nb))
-    _require(packed, "packed", torch.bfloat16)
-    _require(O, "O", torch.float32, (g.H, g.Lq * g.b, g.d))
-    _require(lse, "lse", torch.float32, (g.H, g.Lq * g.b))
-    if slot_hi > packed.shape[0]:
-        raise ValueError("packed holds fewer than slot_hi slots")
+    _require_packed(packed, g, min_slots=slot_hi)
+    _require_outputs((O, lse), g)
     scale = 1.0 / math.sqrt(g.d) if softmax_scale is None else float(softmax_scale)
+    _on_device(Q=Q, mask=mask, slot_of=slot_of, packed=packed, O=O, lse=lse)
     check(load().sparsp_block_sparse_attn_segment_accumulate(ctypes.byref(g), _ptr(Q), _ptr(mask), mask.shape[2],
                                                              _ptr(slot_of), _ptr(packed), int(slot_lo), int(slot_hi),
                                                              scale, _ptr(O), _ptr(lse), _stream(stream)))
+    return O, lse
+
+
+def chunk_plan(seg_offsets: np.ndarray, counts: np.ndarray, placement: np.ndarray, G: int, r: int,
+               chunks_steady: int = 1, chunks_drain: int = 1) -> list[dict]:
+    """The consumption schedule of the payload (sparsp_chunk_plan, host call): a list of chunks
+    {p, h_lo, h_hi, slot_lo, slot_hi, tiles} in execution order.  ``seg_offsets`` int32 [G*H+1] and
+    ``counts`` int32 [H][nb] are host copies of sparsp_demand_union's and sparsp_demand_counts' outputs."""
+    seg = np.ascontiguousarray(seg_offsets, dtype=np.int32)
+    cnt = np.ascontiguousarray(counts, dtype=np.int32)
+    P = np.ascontiguousarray(placement, dtype=np.int32)
+    if cnt.ndim != 2 or cnt.shape[1] != len(P):
+        raise ValueError("counts must be [H][nb] with nb = len(placement)")
+    H, nb = cnt.shape
+    if seg.shape != (G * H + 1,):
+        raise ValueError(f"seg_offsets must hold G*H + 1 = {G * H + 1} entries")
+    cap = G * H
+    buf = (Chunk * cap)()
+    n = ctypes.c_int32(0)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    check(load().sparsp_chunk_plan(seg.ctypes.data_as(i32p), cnt.ctypes.data_as(i32p), P.ctypes.data_as(i32p), G, H, nb,
+                                   r, chunks_steady, chunks_drain, buf, cap, ctypes.byref(n)))
+    return [dict(p=c.p, h_lo=c.h_lo, h_hi=c.h_hi, slot_lo=c.slot_lo, slot_hi=c.slot_hi, tiles=c.tiles)
+            for c in buf[:n.value]]
+
+
+def block_sparse_attn_chunk_accumulate(g: Geometry, Q, mask, slot_of, packed, chunk: dict, O, lse,
+                                       softmax_scale: float | None = None, stream=None):
+    """Fold one chunk of a schedule (heads [h_lo, h_hi), slots [slot_lo, slot_hi)) into the running (O, lse) in
+    place (sparsp_block_sparse_attn_chunk_accumulate); only that head range is launched."""
+    import torch
+    _require(Q, "Q", torch.bfloat16, (g.H, g.Lq * g.b, g.d))
+    _require_mask(mask, g)
+    _require(slot_of, "slot_of", torch.int32, (g.H, g.nb))
+    _require_packed(packed, g, min_slots=chunk["slot_hi"])
+    _require_outputs((O, lse), g)
+    scale = 1.0 / math.sqrt(g.d) if softmax_scale is None else float(softmax_scale)
+    _on_device(Q=Q, mask=mask, slot_of=slot_of, packed=packed, O=O, lse=lse)
+    check(load().sparsp_block_sparse_attn_chunk_accumulate(ctypes.byref(g), _ptr(Q), _ptr(mask), mask.shape[2],
+                                                           _ptr(slot_of), _ptr(packed), int(chunk["slot_lo"]),
+                                                           int(chunk["slot_hi"]), int(chunk["h_lo"]), int(chunk["h_hi"]),
+                                                           scale, _ptr(O), _ptr(lse), _stream(stream)))
     return O, lse
 
 
@@ -192,6 +287,7 @@ def merge_partial(g: Geometry, O, lse, O_part, lse_part, stream=None):
         _require(t, name, torch.float32, (g.H, g.Lq * g.b, g.d))
     for t, name in ((lse, "lse"), (lse_part, "lse_part")):
         _require(t, name, torch.float32, (g.H, g.Lq * g.b))
+    _on_device(O=O, lse=lse, O_part=O_part, lse_part=lse_part)
     check(load().sparsp_merge_partial(ctypes.byref(g), _ptr(O), _ptr(lse), _ptr(O_part), _ptr(lse_part),
                                       _stream(stream)))
     return O, lse
@@ -232,6 +328,7 @@ def permute_blocks(x, pos, b: int, inverse: bool = False, out=None, stream=None)
         out = torch.empty_like(x)
     elif out.shape != x.shape or out.dtype != x.dtype or not out.is_contiguous():
         raise ValueError("out must match x")
+    _on_device(pos=pos, out=out)
     check(load().sparsp_permute_blocks(_ptr(x), _ptr(out), outer, nb, b * C * x.element_size(), _ptr(pos),
                                        1 if inverse else 0, _stream(stream)))
     return out
@@ -241,13 +338,12 @@ def demand_counts(g: Geometry, mask, out=None, stream=None):
     """Access counts of the rank's mask rows (sparsp_demand_counts): int32 [H][nb], the number of local
     query blocks selecting each key block."""
     import torch
-    _require(mask, "mask", torch.uint8)
-    if mask.dim() != 3 or mask.shape[0] != g.H or mask.shape[1] != g.Lq:
-        raise ValueError("mask must be [H][Lq][pitch]")
+    _require_mask(mask, g)
     if out is None:
         out = torch.empty((g.H, g.nb), dtype=torch.int32, device=mask.device)
     else:
         _require(out, "counts", torch.int32, (g.H, g.nb))
+    _on_device(mask=mask, counts=out)
     check(load().sparsp_demand_counts(ctypes.byref(g), _ptr(mask), mask.shape[2], _ptr(out), _stream(stream)))
     return out
 
@@ -285,6 +381,7 @@ def pool_blocks(g: Geometry, X, block_ids=None, out=None, stream=None):
         out = torch.empty((g.H, n, g.d), dtype=torch.float32, device=X.device)
     else:
         _require(out, "pooled", torch.float32, (g.H, n, g.d))
+    _on_device(X=X, block_ids=block_ids, pooled=out)
     check(load().sparsp_pool_blocks(ctypes.byref(g), _ptr(X), n, _ptr(block_ids), _ptr(out), _stream(stream)))
     return out
 
@@ -300,7 +397,8 @@ def materialize_mask(g: Geometry, q_pooled, k_pooled, tau: float, k_min: int, so
     if out is None:
         out = torch.empty((g.H, g.Lq, 64 * g.W), dtype=torch.uint8, device=q_pooled.device)
     else:
-        _require(out, "mask", torch.uint8)
+        _require_mask(out, g)
+    _on_device(q_pooled=q_pooled, k_pooled=k_pooled, mask=out)
     check(load().sparsp_materialize_mask(ctypes.byref(g), _ptr(q_pooled), _ptr(k_pooled), scale, float(tau),
                                          int(k_min), _ptr(out), out.shape[2], _stream(stream)))
     return out

@@ -28,12 +28,20 @@ EXPORTS = (
     "sparsp_block_sparse_attn_segment",
     "sparsp_merge_partial",
     "sparsp_block_sparse_attn_segment_accumulate",
+    "sparsp_chunk_plan",
+    "sparsp_block_sparse_attn_chunk_accumulate",
     "sparsp_placement_permutation",
     "sparsp_permute_blocks",
     "sparsp_demand_counts",
     "sparsp_comm_volume",
     "sparsp_pool_blocks",
     "sparsp_materialize_mask",
+)
+# every symbol include/sparsp_measure.h declares (measurement support)
+MEASURE_EXPORTS = (
+    "sparsp_clock_sampler",
+    "sparsp_wall_timestamp",
+    "sparsp_wall_clock_khz",
 )
 
 
@@ -49,6 +57,13 @@ class Geometry(ctypes.Structure):
     @property
     def W(self) -> int:
         return -(-self.nb // 64)
+
+
+class Chunk(ctypes.Structure):
+    """sparsp_chunk: heads [h_lo, h_hi) of source rank p's segment = packed slots [slot_lo, slot_hi)."""
+    _fields_ = [("p", ctypes.c_int32), ("h_lo", ctypes.c_int32), ("h_hi", ctypes.c_int32),
+                ("slot_lo", ctypes.c_int32), ("slot_hi", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("tiles", ctypes.c_int64)]
 
 
 class SparspError(RuntimeError):
@@ -89,6 +104,10 @@ def load() -> ctypes.CDLL:
     lib.sparsp_block_sparse_attn_segment.argtypes = [gp, P, P, i64, P, P, i32, i32, f32, P, P, P]
     lib.sparsp_block_sparse_attn_segment_accumulate.restype = i32
     lib.sparsp_block_sparse_attn_segment_accumulate.argtypes = [gp, P, P, i64, P, P, i32, i32, f32, P, P, P]
+    lib.sparsp_chunk_plan.restype = i32
+    lib.sparsp_chunk_plan.argtypes = [i32p, i32p, i32p, i32, i32, i32, i32, i32, i32, P, i32, i32p]
+    lib.sparsp_block_sparse_attn_chunk_accumulate.restype = i32
+    lib.sparsp_block_sparse_attn_chunk_accumulate.argtypes = [gp, P, P, i64, P, P, i32, i32, i32, i32, f32, P, P, P]
     lib.sparsp_merge_partial.restype = i32
     lib.sparsp_merge_partial.argtypes = [gp, P, P, P, P, P]
     lib.sparsp_placement_permutation.restype = i32
@@ -103,6 +122,12 @@ def load() -> ctypes.CDLL:
     lib.sparsp_pool_blocks.argtypes = [gp, P, i32, P, P, P]
     lib.sparsp_materialize_mask.restype = i32
     lib.sparsp_materialize_mask.argtypes = [gp, P, P, f32, f32, i32, P, i64, P]
+    lib.sparsp_clock_sampler.restype = i32
+    lib.sparsp_clock_sampler.argtypes = [P, i32, i32, P]
+    lib.sparsp_wall_timestamp.restype = i32
+    lib.sparsp_wall_timestamp.argtypes = [P, P]
+    lib.sparsp_wall_clock_khz.restype = i32
+    lib.sparsp_wall_clock_khz.argtypes = [i32p]
     _lib = lib
     return lib
 

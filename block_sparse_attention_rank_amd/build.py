@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsparsp.so")
-SOURCES = ["api.hip", "union_compact.hip", "pack.hip", "attention.hip", "merge.hip", "permute.hip", "accounting.hip", "materialize.hip"]
+SOURCES = ["api.hip", "union_compact.hip", "pack.hip", "attention.hip", "merge.hip", "permute.hip", "accounting.hip",
+           "materialize.hip", "measure.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

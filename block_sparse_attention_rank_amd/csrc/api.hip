@@ -137,21 +137,25 @@ int32_t sparsp_pack_kv(const sparsp_geometry* geom, const uint16_t* K, const uin
 
 namespace {
 
-// Shared checks and launch of the attention entry points over the slot range [slot_lo, slot_hi).
+// Shared checks and launch of the attention entry points over the slot range [slot_lo, slot_hi) and the heads
+// [h_lo, h_hi) (all heads when h_hi < 0).
 int32_t attention_call(const char* fn, const sparsp_geometry* geom, const uint16_t* Q, const uint8_t* mask,
                        int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed, int32_t slot_lo,
-                       int32_t slot_hi, float softmax_scale, float* O, float* lse, void* stream, int accumulate = 0) {
+                       int32_t slot_hi, float softmax_scale, float* O, float* lse, void* stream, int accumulate = 0,
+                       int32_t h_lo = 0, int32_t h_hi = -1) {
   sparsp::Dims d;
   int32_t st = check_geometry(geom, fn, &d);
   if (st) return st;
+  if (h_hi < 0) h_hi = d.H;
+  if (h_lo < 0 || h_hi > d.H || h_lo > h_hi) return fail(SPARSP_ERR_INVALID, fn, "need 0 <= h_lo <= h_hi <= H");
   if ((st = check_mask(d, mask, mask_pitch, fn))) return st;
   if (d.Lq > 0 && (!Q || !slot_of || !packed || !O || !lse)) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
   if (!isfinite(softmax_scale) || !(softmax_scale > 0.f))
     return fail(SPARSP_ERR_INVALID, fn, "softmax_scale must be finite and positive");
   if ((Q && !aligned16(Q)) || (packed && !aligned16(packed)) || (O && !aligned16(O)))
     return fail(SPARSP_ERR_INVALID, fn, "Q, packed and O must be 16-byte aligned");
-  return hip_status(sparsp::launch_attention(d, Q, mask, mask_pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale,
-                                             O, lse, accumulate, reinterpret_cast<hipStream_t>(stream)),
+  return hip_status(sparsp::launch_attention(d, Q, mask, mask_pitch, slot_of, packed, slot_lo, slot_hi, h_lo, h_hi,
+                                             softmax_scale, O, lse, accumulate, reinterpret_cast<hipStream_t>(stream)),
                     fn);
 }
 
@@ -184,6 +188,65 @@ int32_t sparsp_block_sparse_attn_segment_accumulate(const sparsp_geometry* geom,
   if (slot_lo < 0 || slot_hi < slot_lo) return fail(SPARSP_ERR_INVALID, fn, "need 0 <= slot_lo <= slot_hi");
   return attention_call(fn, geom, Q, mask, mask_pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse,
                         stream, 1);
+}
+
+int32_t sparsp_block_sparse_attn_chunk_accumulate(const sparsp_geometry* geom, const uint16_t* Q, const uint8_t* mask,
+                                                  int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed,
+                                                  int32_t slot_lo, int32_t slot_hi, int32_t h_lo, int32_t h_hi,
+                                                  float softmax_scale, float* O, float* lse, void* stream) {
+  static const char* fn = "sparsp_block_sparse_attn_chunk_accumulate";
+  if (slot_lo < 0 || slot_hi < slot_lo) return fail(SPARSP_ERR_INVALID, fn, "need 0 <= slot_lo <= slot_hi");
+  if (h_lo < 0 || h_hi < h_lo) return fail(SPARSP_ERR_INVALID, fn, "need 0 <= h_lo <= h_hi <= H");
+  return attention_call(fn, geom, Q, mask, mask_pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse,
+                        stream, 1, h_lo, h_hi);
+}
+
+int32_t sparsp_chunk_plan(const int32_t* seg_offsets, const int32_t* counts, const int32_t* placement, int32_t G,
+                          int32_t H, int32_t nb, int32_t r, int32_t chunks_steady, int32_t chunks_drain,
+                          sparsp_chunk* chunks, int32_t capacity, int32_t* n_chunks) {
+  static const char* fn = "sparsp_chunk_plan";
+  if (!seg_offsets || !counts || !placement || !n_chunks) return fail(SPARSP_ERR_INVALID, fn, "NULL pointer");
+  if (G < 1 || G > sparsp::kMaxRanks || H < 1 || nb < 1) return fail(SPARSP_ERR_INVALID, fn, "bad G, H or nb");
+  if (r < 0 || r >= G) return fail(SPARSP_ERR_INVALID, fn, "r must lie in [0, G)");
+  if (chunks_steady < 1 || chunks_drain < 1) return fail(SPARSP_ERR_INVALID, fn, "chunk counts must be >= 1");
+  for (int32_t j = 0; j < nb; ++j)
+    if (placement[j] < 0 || placement[j] >= G) return fail(SPARSP_ERR_INVALID, fn, "placement value outside [0, G)");
+  for (int32_t i = 0; i < G * H; ++i)
+    if (seg_offsets[i + 1] < seg_offsets[i] || seg_offsets[i] < 0)
+      return fail(SPARSP_ERR_INVALID, fn, "seg_offsets must be a non-decreasing prefix from >= 0");
+  // Selected tiles per (source rank, head): the access counts summed over the blocks each rank owns.
+  std::vector<int64_t> tiles((size_t)G * H, 0);
+  for (int32_t h = 0; h < H; ++h)
+    for (int32_t j = 0; j < nb; ++j) tiles[(size_t)placement[j] * H + h] += counts[(size_t)h * nb + j];
+  std::vector<sparsp_chunk> plan;
+  for (int32_t k = 0; k < G; ++k) {
+    const int32_t p = (r + k) % G;
+    // The local segment stays whole; the final remote segment uses the drain count, the others the steady count.
+    int32_t c = k == 0 ? 1 : (k == G - 1 ? chunks_drain : chunks_steady);
+    if (c > H) c = H;
+    const size_t first = plan.size();
+    for (int32_t i = 0; i < c; ++i) {
+      sparsp_chunk ch;
+      ch.p = p;
+      ch.h_lo = (int32_t)((int64_t)i * H / c);
+      ch.h_hi = (int32_t)((int64_t)(i + 1) * H / c);
+      ch.slot_lo = seg_offsets[p * H + ch.h_lo];
+      ch.slot_hi = seg_offsets[p * H + ch.h_hi];
+      ch.reserved = 0;
+      ch.tiles = 0;
+      for (int32_t h = ch.h_lo; h < ch.h_hi; ++h) ch.tiles += tiles[(size_t)p * H + h];
+      if (ch.slot_hi > ch.slot_lo) plan.push_back(ch);
+    }
+    // Within the segment: most tiles first, so its chunk with the highest sparsity runs last (ties: lower
+    // heads first: a stable insertion sort).
+    for (size_t a = first + 1; a < plan.size(); ++a)
+      for (size_t b = a; b > first && plan[b - 1].tiles < plan[b].tiles; --b) std::swap(plan[b - 1], plan[b]);
+  }
+  *n_chunks = (int32_t)plan.size();
+  if ((int32_t)plan.size() > capacity || (!plan.empty() && !chunks))
+    return fail(SPARSP_ERR_INVALID, fn, "chunk capacity too small");
+  for (size_t i = 0; i < plan.size(); ++i) chunks[i] = plan[i];
+  return SPARSP_OK;
 }
 
 int32_t sparsp_merge_partial(const sparsp_geometry* geom, float* O, float* lse, const float* O_part,

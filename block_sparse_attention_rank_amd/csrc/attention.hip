@@ -266,7 +266,7 @@ template <int D, int B>
 __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) void bsa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint8_t* __restrict__ mask, int64_t pitch,
     const int32_t* __restrict__ slot_of, const uint16_t* __restrict__ packed, int slot_lo, int slot_hi, float scale_log2,
-    int H, int Lq, int nb, int N, float* __restrict__ O, float* __restrict__ lse, int accumulate) {
+    int h_lo, int n_heads, int Lq, int nb, int N, float* __restrict__ O, float* __restrict__ lse, int accumulate) {
   using T = Tile<D, B>;
   // Separate double buffers for K and V^T.  The work is cut into units of 32 keys (two per stage); the
   // scores of unit u + 1 are computed while unit u is turned into probabilities, and then unit u is
@@ -279,8 +279,9 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   __shared__ int sWaveCnt[T::NW];
 
   const int wid = xcd_chunked<kXcdChunk>(blockIdx.x);
-  if (wid >= H * Lq) return;  // padding of the grid to whole chunk rounds
-  const int h = wid / Lq, k = wid - h * Lq;
+  if (wid >= n_heads * Lq) return;  // padding of the grid to whole chunk rounds
+  const int hh = wid / Lq, k = wid - hh * Lq;
+  const int h = h_lo + hh;
   const int t = threadIdx.x, lane = t % 64;
   const int wave = __builtin_amdgcn_readfirstlane(t / 64);
   const int qr = lane % 32, half = lane / 32;
@@ -540,14 +541,16 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 template <int D, int B>
 hipError_t launch_attention_t(const Dims& g, const uint16_t* Q, const uint8_t* mask, int64_t pitch,
                               const int32_t* slot_of, const uint16_t* packed, int32_t slot_lo, int32_t slot_hi,
-                              float softmax_scale, float* O, float* lse, int accumulate, hipStream_t stream) {
-  const int64_t items = (int64_t)g.H * g.Lq;
+                              int h_lo, int h_hi, float softmax_scale, float* O, float* lse, int accumulate,
+                              hipStream_t stream) {
+  const int64_t items = (int64_t)(h_hi - h_lo) * g.Lq;
   if (items == 0) return hipSuccess;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
   constexpr int64_t round = (int64_t)kXcds * kXcdChunk;
   const int64_t grid = (items + round - 1) / round * round;
   hipLaunchKernelGGL((bsa_fwd_kernel<D, B>), dim3((unsigned)grid), dim3(2 * B), 0, stream, Q, mask, pitch,
-                     slot_of, packed, slot_lo, slot_hi, scale_log2, g.H, g.Lq, g.nb, g.N, O, lse, accumulate);
+                     slot_of, packed, slot_lo, slot_hi, scale_log2, h_lo, h_hi - h_lo, g.Lq, g.nb, g.N, O, lse,
+                     accumulate);
   return hipGetLastError();
 }
 
@@ -555,18 +558,19 @@ hipError_t launch_attention_t(const Dims& g, const uint16_t* Q, const uint8_t* m
 
 hipError_t launch_attention(const Dims& g, const uint16_t* Q, const uint8_t* mask, int64_t pitch,
                             const int32_t* slot_of, const uint16_t* packed, int32_t slot_lo, int32_t slot_hi,
-                            float softmax_scale, float* O, float* lse, int accumulate, hipStream_t stream) {
+                            int32_t h_lo, int32_t h_hi, float softmax_scale, float* O, float* lse, int accumulate,
+                            hipStream_t stream) {
   if (g.d == 128 && g.b == 128)
-    return launch_attention_t<128, 128>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse, accumulate,
-                                        stream);
+    return launch_attention_t<128, 128>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, h_lo, h_hi, softmax_scale,
+                                        O, lse, accumulate, stream);
   if (g.d == 64 && g.b == 64)
-    return launch_attention_t<64, 64>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse, accumulate,
-                                      stream);
+    return launch_attention_t<64, 64>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, h_lo, h_hi, softmax_scale,
+                                      O, lse, accumulate, stream);
   if (g.d == 128 && g.b == 64)
-    return launch_attention_t<128, 64>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse, accumulate,
-                                       stream);
-  return launch_attention_t<64, 128>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, softmax_scale, O, lse, accumulate,
-                                     stream);
+    return launch_attention_t<128, 64>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, h_lo, h_hi, softmax_scale,
+                                       O, lse, accumulate, stream);
+  return launch_attention_t<64, 128>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, h_lo, h_hi, softmax_scale,
+                                     O, lse, accumulate, stream);
 }
 
 }  // namespace sparsp

@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const uint16_t* __re
                                                             const int32_t* __restrict__ seg_offsets, int GH,
                                                             const int32_t* __restrict__ slot_block,
                                                             const int32_t* __restrict__ slot_head,
-                                                            int slot_capacity, int nb,
+                                                            int slot_capacity, int H, int nb,
                                                             uint16_t* __restrict__ packed) {
   constexpr int kSub = (B / 8) * (D / 8);         // 8 x 8 sub-tiles per block
   constexpr int kSlotsPerWg = kPackThreads / kSub;  // 1, 2 or 4
@@ -64,6 +64,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(const uint16_t* __re
   if (s >= S) return;
   const int u = threadIdx.x % kSub;
   const int h = slot_head[s], j = slot_block[s];
+  if ((unsigned)h >= (unsigned)H || (unsigned)j >= (unsigned)nb) return;  // inconsistent slot arrays: skip the slot
   const int64_t src = ((int64_t)h * nb + j) * B * D;
   uint16_t* dst = packed + (int64_t)s * kSlotElems;
 
@@ -110,7 +111,7 @@ hipError_t launch_pack_t(const Dims& g, const uint16_t* K, const uint16_t* V, co
   const unsigned grid = (unsigned)(((cap + kSlotsPerWg - 1) / kSlotsPerWg + round - 1) / round * round);
   if (grid == 0) return hipSuccess;
   hipLaunchKernelGGL((pack_kernel<D, B>), dim3(grid), dim3(kPackThreads), 0, stream, K, V, seg_offsets, g.G * g.H,
-                     slot_block, slot_head, (int)cap, g.nb, packed);
+                     slot_block, slot_head, (int)cap, g.H, g.nb, packed);
   return hipGetLastError();
 }
 

@@ -29,11 +29,13 @@ hipError_t launch_compact(const Dims& g, const int32_t* placement, const uint64_
 hipError_t launch_pack(const Dims& g, const uint16_t* K, const uint16_t* V, const int32_t* seg_offsets,
                        const int32_t* slot_block, const int32_t* slot_head, int32_t slot_capacity,
                        uint16_t* packed, hipStream_t stream);
-// Attention over the selected blocks whose slot lies in [slot_lo, slot_hi).  accumulate = 0 writes (O, lse);
-// 1 folds the result into the running (O, lse) by their log-sum-exp (rows without keys in range untouched).
+// Attention of heads [h_lo, h_hi) over the selected blocks whose slot lies in [slot_lo, slot_hi); only those
+// heads' (head, query block) items are launched.  accumulate = 0 writes (O, lse); 1 folds the result into the
+// running (O, lse) by their log-sum-exp (rows without keys in range untouched).
 hipError_t launch_attention(const Dims& g, const uint16_t* Q, const uint8_t* mask, int64_t pitch,
                             const int32_t* slot_of, const uint16_t* packed, int32_t slot_lo, int32_t slot_hi,
-                            float softmax_scale, float* O, float* lse, int accumulate, hipStream_t stream);
+                            int32_t h_lo, int32_t h_hi, float softmax_scale, float* O, float* lse, int accumulate,
+                            hipStream_t stream);
 // Fold a partial (O_part, lse_part) into (O, lse), rows of d floats.
 hipError_t launch_merge(int64_t rows, int d, float* O, float* lse, const float* O_part, const float* lse_part,
                         hipStream_t stream);

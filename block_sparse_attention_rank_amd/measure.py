@@ -1,0 +1,60 @@
+"""Shader-clock measurement around device work (include/sparsp_measure.h): a sampler kernel on a side stream
+records (shader clock, wall clock) pairs while the measured kernels run on the main stream, and two wall-clock
+timestamps in the main stream's order mark the window whose average shader clock is reported."""
+from __future__ import annotations
+
+import ctypes
+
+from ._lib import check, load
+
+
+class ClockWindow:
+    """Average shader clock over a window of one stream's work.
+
+        cw = ClockWindow(max_seconds=0.5)
+        cw.start(stream); ...launches on stream...; cw.stop(stream)
+        ghz = cw.result()["ghz"]
+
+    The sampler takes a sample every ``interval_us`` microseconds for at most ``max_seconds`` and then exits by
+    itself; the window must end before it does (result() reports how many samples fell inside)."""
+
+    def __init__(self, max_seconds: float = 0.5, interval_us: float = 20.0):
+        import torch
+        lib = load()
+        khz = ctypes.c_int32(0)
+        check(lib.sparsp_wall_clock_khz(ctypes.byref(khz)))
+        self.khz = khz.value
+        self.interval = max(1, int(round(interval_us * 1e-6 * self.khz * 1e3)))
+        self.n = max(2, int(max_seconds * self.khz * 1e3 / self.interval) + 1)
+        self.samples = torch.zeros(2 * self.n, dtype=torch.int64, device="cuda")
+        self.ts = torch.zeros(2, dtype=torch.int64, device="cuda")
+        self.side = torch.cuda.Stream()            # default priority
+        self._lib = lib
+
+    def start(self, stream=None) -> None:
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        self.side.wait_stream(s)                   # the sampler starts after the work queued so far
+        check(self._lib.sparsp_clock_sampler(ctypes.c_void_p(self.samples.data_ptr()), self.n, self.interval,
+                                             ctypes.c_void_p(self.side.cuda_stream)))
+        check(self._lib.sparsp_wall_timestamp(ctypes.c_void_p(self.ts.data_ptr()), ctypes.c_void_p(s.cuda_stream)))
+
+    def stop(self, stream=None) -> None:
+        import torch
+        s = stream if stream is not None else torch.cuda.current_stream()
+        check(self._lib.sparsp_wall_timestamp(ctypes.c_void_p(self.ts.data_ptr() + 8), ctypes.c_void_p(s.cuda_stream)))
+
+    def result(self) -> dict:
+        import numpy as np
+        import torch
+        torch.cuda.synchronize()
+        smp = self.samples.cpu().numpy().reshape(-1, 2)
+        t0, t1 = (int(x) for x in self.ts.cpu().numpy())
+        smp = smp[smp[:, 1] > 0]
+        inside = smp[(smp[:, 1] >= t0) & (smp[:, 1] <= t1)]
+        out = dict(samples_in_window=int(len(inside)), window_us=round((t1 - t0) / self.khz * 1e3, 1), ghz=None)
+        if len(inside) >= 2:
+            dc = float(inside[-1, 0] - inside[0, 0])
+            dw = float(inside[-1, 1] - inside[0, 1])
+            out["ghz"] = round(dc / dw * self.khz * 1e3 / 1e9, 4)
+        return out

@@ -19,11 +19,15 @@
  *   4. sparsp_block_sparse_attn   -- softmax(Q K^T / sqrt(d)) V (section 2.2) over the selected key
  *                                    blocks only, with an online softmax (section 2.3), reading K/V
  *                                    from the compacted buffer.
- *   5. sparsp_block_sparse_attn_segment, sparsp_merge_partial, sparsp_block_sparse_attn_segment_accumulate
+ *   5. sparsp_block_sparse_attn_segment, sparsp_merge_partial, sparsp_block_sparse_attn_segment_accumulate,
+ *      sparsp_chunk_plan, sparsp_block_sparse_attn_chunk_accumulate
  *                                 -- the same attention restricted to one range of packed slots (one
  *                                    source rank's segment, consumed as it arrives: sections 5.1 and
  *                                    7), the log-sum-exp merge of such partial results (section 2.3's
- *                                    online softmax across pieces of KV), and both fused in one call.
+ *                                    online softmax across pieces of KV), both fused in one call, and
+ *                                    the consumption schedule of section 7: segments cut into head
+ *                                    chunks, finer for the final remote segment (7.1), the chunk with the
+ *                                    highest sparsity of a segment last (7.2).
  *   6. sparsp_placement_permutation, sparsp_permute_blocks
  *                                 -- the placement realised as a permutation of whole blocks into
  *                                    rank-major order, applied to hidden states and undone afterwards
@@ -63,7 +67,7 @@
 extern "C" {
 #endif
 
-#define SPARSP_ABI_VERSION 6
+#define SPARSP_ABI_VERSION 7
 
 typedef enum sparsp_status {
   SPARSP_OK = 0,
@@ -137,7 +141,8 @@ int32_t sparsp_demand_union(const sparsp_geometry* g, const uint8_t* mask, int64
  *   packed       [slot_capacity][2][b*d] bf16.  Slot s = (h, j) = (slot_head[s], slot_block[s]) holds
  *                  part 0: K[h, j*b + t, c] at t*d + c        (the K block, token-major, b x d)
  *                  part 1: V[h, j*b + t, c] at c*b + t        (the V block transposed, d x b)
- *                for every s < min(S, slot_capacity); other slots are left untouched  (written)
+ *                for every s < min(S, slot_capacity); other slots are left untouched, and so is a slot
+ *                whose slot_head or slot_block lies outside [0, H) or [0, nb)            (written)
  * Errors: SPARSP_ERR_INVALID (null pointers, slot_capacity < 1, misaligned K/V/packed: 16 bytes);
  * SPARSP_ERR_UNSUPPORTED (d or b outside {64, 128}).
  */
@@ -199,6 +204,55 @@ int32_t sparsp_block_sparse_attn_segment_accumulate(const sparsp_geometry* g, co
                                                     int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed,
                                                     int32_t slot_lo, int32_t slot_hi, float softmax_scale, float* O,
                                                     float* lse, void* stream);
+
+/*
+ * One chunk of a consumption schedule (section 7): heads [h_lo, h_hi) of source rank p's segment, which are the
+ * packed slots [slot_lo, slot_hi) (each head of a segment is contiguous), carrying `tiles` selected (head, local
+ * query block, key block) triples of this rank's mask.
+ */
+typedef struct sparsp_chunk {
+  int32_t p;
+  int32_t h_lo, h_hi;
+  int32_t slot_lo, slot_hi;
+  int32_t reserved;  /* 0 */
+  int64_t tiles;
+} sparsp_chunk;
+
+/*
+ * The consumption schedule of the payload (section 7, Figure 11).  HOST pointers.  Segments are consumed in
+ * ring order p = r, r+1, ..., r+G-1 (mod G): the local segment first and whole (section 7.1: it needs no
+ * communication), every remote segment cut into `chunks_steady` head chunks except the final remote segment,
+ * which is cut into `chunks_drain` (section 7.1: finer chunks where the pipeline drains).  A segment of c
+ * chunks (c clamped to H) splits the heads into [floor(i*H/c), floor((i+1)*H/c)), i = 0..c-1.  Inside a
+ * segment the chunks are ordered by decreasing tile count, ties by ascending h_lo, so the chunk with the
+ * highest sparsity runs last (section 7.2).  Chunks without slots are left out.
+ *   seg_offsets  [G*H + 1] int32, as written by sparsp_demand_union                              (read)
+ *   counts       [H][nb] int32, as written by sparsp_demand_counts for the same mask             (read)
+ *   placement    [nb] int32, P(j) in [0, G)                                                       (read)
+ *   chunks       [capacity] sparsp_chunk: the schedule in execution order                         (written)
+ *   n_chunks     number of chunks (written also when capacity is too small; at most G*H)
+ * Folding every chunk with sparsp_block_sparse_attn_chunk_accumulate, in this order or any other, gives the
+ * result of sparsp_block_sparse_attn up to rounding.
+ * Errors: SPARSP_ERR_INVALID for null pointers, G outside [1, 64], H < 1, nb < 1, r outside [0, G), chunk
+ * counts < 1, a placement value outside [0, G), decreasing seg_offsets, or capacity below the chunk count
+ * (then nothing is written to chunks).
+ */
+int32_t sparsp_chunk_plan(const int32_t* seg_offsets, const int32_t* counts, const int32_t* placement, int32_t G,
+                          int32_t H, int32_t nb, int32_t r, int32_t chunks_steady, int32_t chunks_drain,
+                          sparsp_chunk* chunks, int32_t capacity, int32_t* n_chunks);
+
+/*
+ * sparsp_block_sparse_attn_segment_accumulate restricted to the heads [h_lo, h_hi): one chunk of a schedule
+ * from sparsp_chunk_plan (section 7.2: attention is partitioned by heads).  Only that head range's (head,
+ * local query block) items are launched; rows of other heads are not touched.  DEVICE pointers; arguments as
+ * for sparsp_block_sparse_attn_segment_accumulate.
+ * Errors: as for sparsp_block_sparse_attn_segment_accumulate; SPARSP_ERR_INVALID also unless
+ * 0 <= h_lo <= h_hi <= H.
+ */
+int32_t sparsp_block_sparse_attn_chunk_accumulate(const sparsp_geometry* g, const uint16_t* Q, const uint8_t* mask,
+                                                  int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed,
+                                                  int32_t slot_lo, int32_t slot_hi, int32_t h_lo, int32_t h_hi,
+                                                  float softmax_scale, float* O, float* lse, void* stream);
 
 /*
  * Fold a partial attention result over one key set into a running result over a disjoint key set (section

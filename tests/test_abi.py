@@ -17,8 +17,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sparsp.h")
 
 
-def _declared_symbols():
-    text = open(HEADER).read()
+MEASURE_HEADER = os.path.join(ROOT, "include", "sparsp_measure.h")
+
+
+def _declared_symbols(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(sparsp_[a-z_]+)\s*\(", text)))
 
@@ -29,11 +32,26 @@ def test_library_exports_every_declared_symbol():
     assert set(declared) == set(_lib.EXPORTS)
     for name in declared:
         assert hasattr(lib, name), name
+    measure = _declared_symbols(MEASURE_HEADER)
+    assert set(measure) == set(_lib.MEASURE_EXPORTS)
+    for name in measure:
+        assert hasattr(lib, name), name
+
+
+def test_measure_argument_checks():
+    lib = bsa.load()
+    E = _lib.SPARSP_ERR_INVALID
+    assert lib.sparsp_clock_sampler(None, 4, 10, None) == E
+    assert lib.sparsp_clock_sampler(FAKE, 1, 10, None) == E
+    assert lib.sparsp_clock_sampler(FAKE, 4, 0, None) == E
+    assert lib.sparsp_clock_sampler(FAKE, 1 << 20, 1 << 20, None) == E                 # unbounded run time
+    assert lib.sparsp_wall_timestamp(None, None) == E
+    assert lib.sparsp_wall_clock_khz(None) == E
 
 
 def test_version_and_status_strings():
     lib = bsa.load()
-    assert lib.sparsp_abi_version() == 6
+    assert lib.sparsp_abi_version() == 7
     assert lib.sparsp_status_string(0) == b"ok"
     assert lib.sparsp_status_string(1) == b"invalid argument"
     assert lib.sparsp_status_string(2) == b"unsupported configuration"
@@ -271,3 +289,103 @@ def test_binding_fails_loudly_without_the_library(tmp_path):
     env = dict(os.environ, SPARSP_LIB=str(tmp_path / "nope.so"))
     out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True)
     assert out.stdout.strip() == "raised True", out.stdout + out.stderr
+
+
+@pytest.mark.parametrize("w_kw", [dict(H=3, d=64, b=64, T=3, HW=320, G=3, r=1, density=0.5),
+                                  dict(H=4, d=128, b=128, T=2, HW=700, G=4, r=2, placement="periodic", density=0.6),
+                                  dict(H=7, d=64, b=64, T=4, HW=256, G=8, r=5, density_range=(0.02, 0.5)),
+                                  dict(H=1, d=64, b=64, T=2, HW=192, G=1, r=0, density=0.4)])
+@pytest.mark.parametrize("steady,drain", [(1, 1), (1, 2), (2, 4), (5, 99)])
+def test_chunk_plan_matches_oracle(w_kw, steady, drain):
+    """The host schedule call against the oracle's plan, on the oracle's compaction and access counts."""
+    from workloads import custom, make_inputs
+    w = custom(**w_kw)
+    inp = make_inputs(w, with_qkv=False)
+    U = O.demand_union(inp["mask"], w.nb)
+    c = O.compact(U, inp["placement"], w.G)
+    counts = O.access_counts(inp["mask"], w.nb).astype(np.int32)
+    got = bsa.chunk_plan(c["seg_offsets"], counts, inp["placement"], w.G, w.r, steady, drain)
+    want = O.chunk_plan(c["seg_offsets"], O.segment_tiles(inp["mask"], inp["placement"], w.G, w.nb), w.G, w.H, w.r,
+                        steady, drain)
+    assert got == want
+
+
+def test_chunk_plan_argument_checks():
+    lib = bsa.load()
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    E = _lib.SPARSP_ERR_INVALID
+    H, G, nb = 2, 2, 4
+    seg = np.array([0, 1, 2, 3, 4], np.int32)
+    cnt = np.ones((H, nb), np.int32)
+    P = np.array([0, 0, 1, 1], np.int32)
+    n = ctypes.c_int32(-1)
+    buf = (_lib.Chunk * 8)()
+    args = lambda **kw: dict(dict(seg=seg, cnt=cnt, P=P, G=G, H=H, nb=nb, r=0, s=1, d=2, cap=8), **kw)  # noqa: E731
+
+    def call(a):
+        return lib.sparsp_chunk_plan(a["seg"].ctypes.data_as(i32p), a["cnt"].ctypes.data_as(i32p),
+                                     a["P"].ctypes.data_as(i32p), a["G"], a["H"], a["nb"], a["r"], a["s"], a["d"], buf,
+                                     a["cap"], ctypes.byref(n))
+    assert call(args()) == _lib.SPARSP_OK and n.value == 3        # local whole + drain of 2
+    assert call(args(r=2)) == E
+    assert call(args(s=0)) == E
+    assert call(args(d=0)) == E
+    assert call(args(G=65)) == E
+    assert call(args(P=np.array([0, 0, 2, 1], np.int32))) == E and b"placement" in lib.sparsp_last_error()
+    assert call(args(seg=np.array([0, 2, 1, 3, 4], np.int32))) == E
+    assert call(args(cap=2)) == E and n.value == 3                  # needed size reported
+    assert lib.sparsp_chunk_plan(None, cnt.ctypes.data_as(i32p), P.ctypes.data_as(i32p), G, H, nb, 0, 1, 1, buf, 8,
+                                 ctypes.byref(n)) == E
+    g = _geom()
+    fn = lib.sparsp_block_sparse_attn_chunk_accumulate
+    assert fn(ctypes.byref(g), FAKE, FAKE, 64, FAKE, FAKE, 0, 4, -1, 1, 0.1, FAKE, FAKE, None) == E   # h_lo < 0
+    assert fn(ctypes.byref(g), FAKE, FAKE, 64, FAKE, FAKE, 0, 4, 1, 3, 0.1, FAKE, FAKE, None) == E    # h_hi > H
+    assert b"h_lo" in lib.sparsp_last_error()
+    assert fn(ctypes.byref(g), FAKE, FAKE, 64, FAKE, FAKE, 0, 4, 2, 1, 0.1, FAKE, FAKE, None) == E    # hi < lo
+    assert fn(ctypes.byref(g), FAKE, FAKE, 64, FAKE, FAKE, 4, 3, 0, 1, 0.1, FAKE, FAKE, None) == E    # slots
+
+
+def test_binding_checks_shapes_before_any_launch():
+    """Wrong shapes of the tensors a kernel reads or writes are refused by the binding (ValueError) before the
+    library is called; on this CPU-only host every tensor is a host tensor, so a shape error must come first."""
+    import torch
+    g = bsa.geometry(H=2, d=64, b=64, N=1000, G=4, r=1, Lq=3)       # nb = 16
+    bf, f32, u8, i32 = torch.bfloat16, torch.float32, torch.uint8, torch.int32
+    Q = torch.zeros((2, 3 * 64, 64), dtype=bf)
+    mask = torch.zeros((2, 3, 16), dtype=u8)
+    slot_of = torch.zeros((2, 16), dtype=i32)
+    packed = torch.zeros((4, 2, 64 * 64), dtype=bf)
+    O_ = torch.zeros((2, 3 * 64, 64), dtype=f32)
+    lse = torch.zeros((2, 3 * 64), dtype=f32)
+
+    def shape_error(fn, *a, **kw):
+        with pytest.raises(ValueError, match="shape|must be \\[|pitch|slots"):
+            fn(*a, **kw)
+
+    shape_error(bsa.block_sparse_attn, g, Q, torch.zeros((2, 2, 16), dtype=u8), slot_of, packed)        # Lq rows
+    shape_error(bsa.block_sparse_attn, g, Q, torch.zeros((2, 3, 8), dtype=u8), slot_of, packed)         # pitch < nb
+    shape_error(bsa.block_sparse_attn, g, Q, torch.zeros((2, 3, 24), dtype=u8), slot_of, packed)        # pitch % 16
+    shape_error(bsa.block_sparse_attn, g, Q, mask, slot_of, torch.zeros((4, 2, 64 * 32), dtype=bf))     # slot size
+    shape_error(bsa.block_sparse_attn, g, Q, mask, slot_of, torch.zeros((4, 64 * 64), dtype=bf))        # dims
+    shape_error(bsa.block_sparse_attn, g, Q, mask, slot_of, packed, out=(O_[:, :64], lse))              # O rows
+    shape_error(bsa.block_sparse_attn, g, Q, mask, slot_of, packed, out=(O_, lse[:1]))                  # lse
+    shape_error(bsa.block_sparse_attn_segment, g, Q, mask, slot_of, packed, 0, 5)                       # > slots
+    shape_error(bsa.block_sparse_attn_segment_accumulate, g, Q, mask, slot_of, packed, 0, 2, O_[:1], lse)
+    shape_error(bsa.block_sparse_attn_chunk_accumulate, g, Q, mask, slot_of, packed,
+                dict(slot_lo=0, slot_hi=9, h_lo=0, h_hi=1), O_, lse)
+    u = bsa.UnionResult(demand=torch.zeros((2, 1), dtype=torch.int64), seg_offsets=torch.zeros(9, dtype=i32),
+                        slot_block=torch.zeros(32, dtype=i32), slot_head=torch.zeros(32, dtype=i32),
+                        slot_of=slot_of)
+    K = torch.zeros((2, 16 * 64, 64), dtype=bf)
+    shape_error(bsa.pack_kv, g, K, K, u, out=torch.zeros((4, 2, 100), dtype=bf))
+    bad_u = bsa.UnionResult(demand=u.demand, seg_offsets=torch.zeros(8, dtype=i32), slot_block=u.slot_block,
+                            slot_head=u.slot_head, slot_of=slot_of)
+    shape_error(bsa.pack_kv, g, K, K, bad_u)
+    shape_error(bsa.demand_union, g, torch.zeros((2, 3, 8), dtype=u8), torch.zeros(16, dtype=i32))
+    shape_error(bsa.demand_union, g, mask, torch.zeros(16, dtype=i32), out=bad_u)
+    shape_error(bsa.demand_counts, g, torch.zeros((1, 3, 16), dtype=u8))
+    shape_error(bsa.materialize_mask, g, torch.zeros((2, 3, 64), dtype=f32), torch.zeros((2, 16, 64), dtype=f32),
+                0.9, 1, out=torch.zeros((2, 3, 8), dtype=u8))
+    # the right shapes pass the shape checks and stop at the device check
+    with pytest.raises(ValueError, match="device"):
+        bsa.block_sparse_attn(g, Q, mask, slot_of, packed, out=(O_, lse))
