@@ -1,9 +1,11 @@
 """Build libsparsp.so (the C-ABI library with its gfx950 kernels) in-tree with hipcc.
 
-    python -m block_sparse_attention_rank_amd.build [--verbose]
+    python -m block_sparse_attention_rank_amd.build [--verbose] [--no-asan]
 
 Each HIP translation unit is compiled to an object under ``_build/`` in parallel, then linked into
-``block_sparse_attention_rank_amd/libsparsp.so``.  Always rebuilds.
+``block_sparse_attention_rank_amd/libsparsp.so``.  A second copy whose host code is built with
+AddressSanitizer (the device code is not instrumented) goes to ``_build/asan/libsparsp_asan.so``; the CPU
+tests load it into a child process to check the host-side calls.  Always rebuilds.
 """
 from __future__ import annotations
 
@@ -18,6 +20,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsparsp.so")
+ASAN_DIR = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_DIR, "libsparsp_asan.so")
+# host code only: every sanitizer flag is scoped to the host pass
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g", "-O1"]
 SOURCES = ["api.hip", "union_compact.hip", "pack.hip", "attention.hip", "merge.hip", "permute.hip", "accounting.hip",
            "materialize.hip", "measure.hip"]
 ARCH = "gfx950"
@@ -74,6 +80,39 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
     return LIB
 
 
+def build_asan(verbose: bool = False) -> str:
+    """The library with AddressSanitizer on its host code (argument checks, the host calls)."""
+    cc = hipcc()
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    flags = [f for f in COMMON_FLAGS if f != "-O3"] + ASAN_FLAGS
+    objs, jobs = [], []
+    for src in SOURCES:
+        obj = os.path.join(ASAN_DIR, src.replace(".hip", ".o"))
+        objs.append(obj)
+        jobs.append([cc, *flags, "-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(len(jobs)) as ex:
+        for f in [ex.submit(_run, j, verbose) for j in jobs]:
+            f.result()
+    tmp = ASAN_LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address", "-o", tmp, *objs],
+         verbose)
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
+
+
+def asan_runtime() -> str | None:
+    """Path of the compiler's AddressSanitizer runtime (to preload into a process that loads ASAN_LIB)."""
+    for cand in ("/opt/rocm/llvm/bin/clang", shutil.which("clang") or ""):
+        if cand and os.path.exists(cand):
+            res = subprocess.run([cand, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+            path = res.stdout.strip()
+            if res.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+                return path
+    return None
+
+
 if __name__ == "__main__":
     path = build(verbose="--verbose" in sys.argv)
     print(path)
+    if "--no-asan" not in sys.argv:
+        print(build_asan(verbose="--verbose" in sys.argv))

@@ -363,7 +363,7 @@ int32_t sparsp_materialize_mask(const sparsp_geometry* geom, const float* q_pool
   int32_t st = check_geometry(geom, fn, &d);
   if (st) return st;
   if ((st = check_mask(d, mask, mask_pitch, fn))) return st;
-  if (d.nb > sparsp::kMaxSelectBlocks) return fail(SPARSP_ERR_UNSUPPORTED, fn, "nb must be <= 4096");
+  if (d.nb > sparsp::kMaxSelectBlocks) return fail(SPARSP_ERR_UNSUPPORTED, fn, "nb must be <= 16384");
   if (d.H > 65535) return fail(SPARSP_ERR_UNSUPPORTED, fn, "H must be <= 65535");
   if (!(tau >= 0.f && tau <= 1.f)) return fail(SPARSP_ERR_INVALID, fn, "tau must lie in [0, 1]");
   if (k_min < 0) return fail(SPARSP_ERR_INVALID, fn, "k_min must be >= 0");

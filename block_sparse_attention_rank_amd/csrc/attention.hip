@@ -34,7 +34,10 @@
 // denominator share the maximum) and safe in fp32 and bf16.  A unit's row sums reveal when that bound
 // is passed (or a row has no maximum yet); only then is the unit's maximum taken, so the common path
 // has neither a maximum nor a cross-lane step: the two halves of a row exchange maxima
-// (v_permlane32_swap) only when the maximum moves, and their partial sums once at the end.
+// (v_permlane32_swap) only when the maximum moves, and their partial sums once at the end.  The
+// numerator (the P V product) takes the probabilities rounded to bf16, the denominator adds their fp32
+// values: the two differ by the bf16 rounding of each probability (relative 2^-9 at most), well inside the
+// output tolerance.
 #include <math.h>
 
 #include "sparsp_internal.h"
@@ -153,7 +156,7 @@ struct RowState {
   using T = Tile<D, B>;
   f32x16 oacc[T::NDT];
   float m_run;  // maximum the probabilities are taken against (log2-scaled logits)
-  float l_run;  // sum of this lane's bf16-rounded probabilities relative to m_run
+  float l_run;  // sum of this lane's fp32 probabilities relative to m_run (the P V product takes them rounded to bf16)
 };
 
 // A unit is one 32-key group g of a stage.  Its scores S^T = K Q^T come from one MFMA tile:

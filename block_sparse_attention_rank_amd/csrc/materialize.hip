@@ -105,7 +105,8 @@ __device__ __forceinline__ float from_ordered_bits(uint32_t o) {
 }
 
 // NT threads, each keeping PER >= np2 / NT blocks of each of the workgroup's R rows in registers: 256 threads,
-// four blocks and four rows for rows of up to 1024 blocks; 512 threads, eight blocks and two rows above.  The
+// four blocks and four rows for rows of up to 1024 blocks; 512 threads, eight blocks and two rows up to 4096;
+// 1024 threads, one row, eight or sixteen blocks up to 16384.  The
 // R rows (consecutive local query blocks of one head) share every pooled-key read and every reduction.
 template <int D, int NT, int R, int PER>
 __global__ __launch_bounds__(NT) void select_kernel(const float* __restrict__ qp, const float* __restrict__ kp,
@@ -372,7 +373,8 @@ hipError_t launch_select(const Dims& g, const float* q_pooled, const float* k_po
   while (np2 < g.nb) np2 <<= 1;
   // Rows of up to 1024 blocks: 256 threads, four blocks per thread and four rows per workgroup; longer rows
   // (up to 4096 blocks): 512 threads, eight blocks per thread and two rows (1024 threads with one row, or two
-  // and four rows of 1024 threads, measured slower).
+  // and four rows of 1024 threads, measured slower); up to 8192 and 16384 blocks: 1024 threads, one row, eight
+  // or sixteen blocks per thread.
   if (np2 <= 1024) {
     const dim3 grid((unsigned)((g.Lq + 3) / 4), (unsigned)g.H);
     if (g.d == 128)
@@ -381,7 +383,7 @@ hipError_t launch_select(const Dims& g, const float* q_pooled, const float* k_po
     else
       hipLaunchKernelGGL((select_kernel<64, 256, 4, 4>), grid, dim3(256), 0, stream, q_pooled, k_pooled, g.Lq, g.nb, np2,
                          scale, tau, k_min, mask, pitch);
-  } else {
+  } else if (np2 <= 4096) {
     const dim3 grid((unsigned)((g.Lq + 1) / 2), (unsigned)g.H);
     if (g.d == 128)
       hipLaunchKernelGGL((select_kernel<128, 512, 2, 8>), grid, dim3(512), 0, stream, q_pooled, k_pooled, g.Lq, g.nb,
@@ -389,6 +391,23 @@ hipError_t launch_select(const Dims& g, const float* q_pooled, const float* k_po
     else
       hipLaunchKernelGGL((select_kernel<64, 512, 2, 8>), grid, dim3(512), 0, stream, q_pooled, k_pooled, g.Lq, g.nb,
                          np2, scale, tau, k_min, mask, pitch);
+  } else {
+    const dim3 grid((unsigned)g.Lq, (unsigned)g.H);
+    if (np2 <= 8192) {
+      if (g.d == 128)
+        hipLaunchKernelGGL((select_kernel<128, 1024, 1, 8>), grid, dim3(1024), 0, stream, q_pooled, k_pooled, g.Lq, g.nb,
+                           np2, scale, tau, k_min, mask, pitch);
+      else
+        hipLaunchKernelGGL((select_kernel<64, 1024, 1, 8>), grid, dim3(1024), 0, stream, q_pooled, k_pooled, g.Lq, g.nb,
+                           np2, scale, tau, k_min, mask, pitch);
+    } else {
+      if (g.d == 128)
+        hipLaunchKernelGGL((select_kernel<128, 1024, 1, 16>), grid, dim3(1024), 0, stream, q_pooled, k_pooled, g.Lq,
+                           g.nb, np2, scale, tau, k_min, mask, pitch);
+      else
+        hipLaunchKernelGGL((select_kernel<64, 1024, 1, 16>), grid, dim3(1024), 0, stream, q_pooled, k_pooled, g.Lq,
+                           g.nb, np2, scale, tau, k_min, mask, pitch);
+    }
   }
   return hipGetLastError();
 }

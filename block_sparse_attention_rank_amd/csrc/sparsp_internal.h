@@ -50,7 +50,7 @@ hipError_t launch_pool(const Dims& g, const uint16_t* X, int n_blocks, const int
 // Mask rows [H][Lq][pitch] from pooled tiles: Top-p (tau) with a Top-k floor (k_min) over the block scores.
 hipError_t launch_select(const Dims& g, const float* q_pooled, const float* k_pooled, float scale, float tau,
                          int k_min, uint8_t* mask, int64_t pitch, hipStream_t stream);
-constexpr int kMaxSelectBlocks = 4096;
+constexpr int kMaxSelectBlocks = kMaxBlocks;
 
 // Move whole blocks: dst[o][pos[j]] = src[o][j] (inverse = 0) or dst[o][j] = src[o][pos[j]] (inverse = 1).
 hipError_t launch_permute(const void* src, void* dst, int64_t outer, int nb, int64_t block_bytes, const int32_t* pos,

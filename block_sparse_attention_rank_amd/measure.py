@@ -31,12 +31,16 @@ class ClockWindow:
         self.side = torch.cuda.Stream()            # default priority
         self._lib = lib
 
-    def start(self, stream=None) -> None:
+    def start(self, stream=None, lead_cycles: int = 2_000_000) -> None:
+        """Start the sampler beside ``stream``.  The stream first idles ``lead_cycles`` shader cycles (about a
+        millisecond) so that the sampler is running before the window opens."""
         import torch
         s = stream if stream is not None else torch.cuda.current_stream()
         self.side.wait_stream(s)                   # the sampler starts after the work queued so far
         check(self._lib.sparsp_clock_sampler(ctypes.c_void_p(self.samples.data_ptr()), self.n, self.interval,
                                              ctypes.c_void_p(self.side.cuda_stream)))
+        with torch.cuda.stream(s):
+            torch.cuda._sleep(int(lead_cycles))
         check(self._lib.sparsp_wall_timestamp(ctypes.c_void_p(self.ts.data_ptr()), ctypes.c_void_p(s.cuda_stream)))
 
     def stop(self, stream=None) -> None:

@@ -362,7 +362,7 @@ int32_t sparsp_pool_blocks(const sparsp_geometry* g, const uint16_t* X, int32_t 
  * Arithmetic is fp32: a block whose score or prefix weight sits within rounding of the decision may
  * fall either way.
  * Errors: SPARSP_ERR_INVALID (null pointers, bad pitch or alignment, tau outside [0, 1], k_min < 0, a
- * scale that is not finite and > 0); SPARSP_ERR_UNSUPPORTED (d or b outside {64, 128}, nb > 4096,
+ * scale that is not finite and > 0); SPARSP_ERR_UNSUPPORTED (d or b outside {64, 128}, nb > 16384,
  * H > 65535).
  */
 int32_t sparsp_materialize_mask(const sparsp_geometry* g, const float* q_pooled, const float* k_pooled,

@@ -8,11 +8,16 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
-try:  # property tests draw the same examples on every run, so the suite's outcome is reproducible
+try:
+    # Two hypothesis profiles.  "ci" (the default) draws the same examples on every run, so the suite's outcome
+    # is reproducible; "explore" draws new examples (more of them) on every run, for searching:
+    #     HYPOTHESIS_PROFILE=explore python -m pytest tests -m "not gpu" [--hypothesis-seed N]
+    # (--hypothesis-seed replays one exploratory run exactly).
     from hypothesis import settings as _hyp_settings
 
-    _hyp_settings.register_profile("reproducible", derandomize=True)
-    _hyp_settings.load_profile("reproducible")
+    _hyp_settings.register_profile("ci", derandomize=True)
+    _hyp_settings.register_profile("explore", derandomize=False, max_examples=300, database=None)
+    _hyp_settings.load_profile(os.environ.get("HYPOTHESIS_PROFILE", "ci"))
 except ImportError:  # pragma: no cover
     pass
 

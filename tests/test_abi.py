@@ -263,8 +263,8 @@ def test_materialize_argument_checks():
     assert mm(gp, FAKE, FAKE, 0.1, 0.5, 1, FAKE, 8, None) == E                           # pitch < nb
     assert mm(gp, None, FAKE, 0.1, 0.5, 1, FAKE, 64, None) == E
     assert mm(gp, FAKE + 4, FAKE, 0.1, 0.5, 1, FAKE, 64, None) == E                      # misaligned
-    big = _geom(b=64, N=64 * 4097, Lq=1)
-    assert mm(ctypes.byref(big), FAKE, FAKE, 0.1, 0.5, 1, FAKE, 4160, None) == U          # nb > 4096
+    big = _geom(b=64, N=64 * 16385, Lq=1)
+    assert mm(ctypes.byref(big), FAKE, FAKE, 0.1, 0.5, 1, FAKE, 16448, None) == U         # nb > 16384
 
 
 def test_product_path_never_touches_the_oracle():

@@ -112,6 +112,10 @@ CASES = {
     # rows of more than 1024 blocks take the 512-thread, two-row select
     "wide_d64": (custom(H=2, d=64, T=12, HW=6144, b=64, G=8, k_offset_sigma=3.0), 0.9, 16),
     "wide_d128_ragged": (custom(H=1, d=128, T=37, HW=3600, b=128, G=8), 0.5, 4),
+    # rows of more than 4096 blocks take the 1024-thread select (eight, then sixteen blocks per thread)
+    "rows_6k_d64": (custom(H=1, d=64, T=2, HW=64 * 3000, b=64, G=64, r=9, k_offset_sigma=3.0), 0.9, 16),
+    "rows_12k_d128_ragged": (custom(H=1, d=128, T=1, HW=128 * 12000 - 51, b=128, G=64, r=33), 0.85, 8),
+    "rows_16k_d64": (custom(H=1, d=64, T=4, HW=64 * 4096, b=64, G=64, r=60, k_offset_sigma=3.0), 0.5, 32),
 }
 
 
@@ -145,8 +149,6 @@ def test_random_geometries(require_gpu, i):
     """Seeded random geometries (both head dims and block sizes, rows on both sides of 1024 blocks, random
     tau and k_min) under the same validity rules."""
     w, tau, k_min = _random_case(i)
-    if w.nb > 4096:
-        pytest.skip("rows of more than 4096 blocks are refused by the select")
     inp, g, qp, kp, mask = _run(w, tau, k_min)
     w = inp["workload"]
     if len(inp["q_blocks"]) == 0:
