@@ -7,6 +7,53 @@ import ctypes
 
 from ._lib import check, load
 
+# Side stream per measured stream, checked to run beside it.  The HIP runtime maps streams onto a few
+# hardware queues (GPU_MAX_HW_QUEUES, 4 by default); a side stream that shares the measured stream's queue
+# runs the sampler before the window instead of during it.
+_SIDE: dict = {}
+
+
+def _runs_beside(lib, khz: int, main, side) -> bool:
+    """True when a sampler launched on ``side`` takes samples while ``main`` is busy."""
+    import torch
+    interval = max(1, int(round(20e-6 * khz * 1e3)))              # 20 us
+    n = 256                                                       # about 5 ms of sampling
+    samples = torch.zeros(2 * n, dtype=torch.int64, device="cuda")
+    ts = torch.zeros(2, dtype=torch.int64, device="cuda")
+    side.wait_stream(main)
+    check(lib.sparsp_clock_sampler(ctypes.c_void_p(samples.data_ptr()), n, interval,
+                                   ctypes.c_void_p(side.cuda_stream)))
+    with torch.cuda.stream(main):
+        torch.cuda._sleep(1_000_000)
+    check(lib.sparsp_wall_timestamp(ctypes.c_void_p(ts.data_ptr()), ctypes.c_void_p(main.cuda_stream)))
+    with torch.cuda.stream(main):
+        torch.cuda._sleep(1_000_000)
+    check(lib.sparsp_wall_timestamp(ctypes.c_void_p(ts.data_ptr() + 8), ctypes.c_void_p(main.cuda_stream)))
+    torch.cuda.synchronize()
+    smp = samples.cpu().numpy().reshape(-1, 2)
+    t0, t1 = (int(x) for x in ts.cpu().numpy())
+    w = smp[:, 1]
+    return int(((w >= t0) & (w <= t1)).sum()) >= 2
+
+
+def side_stream(main=None):
+    """A stream whose work runs concurrently with ``main`` (the current stream by default)."""
+    import torch
+    main = main if main is not None else torch.cuda.current_stream()
+    key = main.cuda_stream
+    if key not in _SIDE:
+        lib = load()
+        khz = ctypes.c_int32(0)
+        check(lib.sparsp_wall_clock_khz(ctypes.byref(khz)))
+        for _ in range(16):
+            cand = torch.cuda.Stream()             # default priority
+            if _runs_beside(lib, khz.value, main, cand):
+                _SIDE[key] = cand
+                break
+        else:
+            raise RuntimeError("no stream was found that runs beside the measured stream")
+    return _SIDE[key]
+
 
 class ClockWindow:
     """Average shader clock over a window of one stream's work.
@@ -28,7 +75,6 @@ class ClockWindow:
         self.n = max(2, int(max_seconds * self.khz * 1e3 / self.interval) + 1)
         self.samples = torch.zeros(2 * self.n, dtype=torch.int64, device="cuda")
         self.ts = torch.zeros(2, dtype=torch.int64, device="cuda")
-        self.side = torch.cuda.Stream()            # default priority
         self._lib = lib
 
     def start(self, stream=None, lead_cycles: int = 2_000_000) -> None:
@@ -36,9 +82,10 @@ class ClockWindow:
         millisecond) so that the sampler is running before the window opens."""
         import torch
         s = stream if stream is not None else torch.cuda.current_stream()
-        self.side.wait_stream(s)                   # the sampler starts after the work queued so far
+        side = side_stream(s)
+        side.wait_stream(s)                        # the sampler starts after the work queued so far
         check(self._lib.sparsp_clock_sampler(ctypes.c_void_p(self.samples.data_ptr()), self.n, self.interval,
-                                             ctypes.c_void_p(self.side.cuda_stream)))
+                                             ctypes.c_void_p(side.cuda_stream)))
         with torch.cuda.stream(s):
             torch.cuda._sleep(int(lead_cycles))
         check(self._lib.sparsp_wall_timestamp(ctypes.c_void_p(self.ts.data_ptr()), ctypes.c_void_p(s.cuda_stream)))
@@ -49,7 +96,6 @@ class ClockWindow:
         check(self._lib.sparsp_wall_timestamp(ctypes.c_void_p(self.ts.data_ptr() + 8), ctypes.c_void_p(s.cuda_stream)))
 
     def result(self) -> dict:
-        import numpy as np
         import torch
         torch.cuda.synchronize()
         smp = self.samples.cpu().numpy().reshape(-1, 2)
