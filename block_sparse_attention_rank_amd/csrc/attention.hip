@@ -265,6 +265,70 @@ __device__ __forceinline__ void block_sync() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// Exclusive prefix, in thread order, of a per-thread count in 0..4 over the workgroup, and the workgroup's
+// total.  Two barriers; sWaveCnt holds one int per wave.
+template <int NW>
+__device__ __forceinline__ int block_prefix4(int cnt, int lane, int wave, int* sWaveCnt, int& total) {
+  int below = 0, wave_total = 0;
+#pragma unroll
+  for (int bit = 0; bit < 3; ++bit) {
+    const uint64_t bal = __builtin_amdgcn_ballot_w64((cnt >> bit) & 1);
+    below += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u)) << bit;
+    wave_total += __popcll(bal) << bit;
+  }
+  if (lane == 0) sWaveCnt[wave] = wave_total;
+  __syncthreads();
+  int off = below;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int c = sWaveCnt[w];
+    off += w < wave ? c : 0;
+    total += c;
+  }
+  __syncthreads();
+  return off;
+}
+
+// Column of the median selected block of a mask row: the floor(count / 2)-th selected column in ascending
+// order (0 for an empty row).  Threads read kListCols consecutive mask bytes per step with one 32-bit load.
+template <int NT, int NW>
+__device__ int median_column(const uint8_t* mrow, int nb, int t, int lane, int wave, int* sWaveCnt, int* sOut) {
+  auto selected = [&](int j0, int& cnt) {
+    const uint32_t w = j0 < nb ? *reinterpret_cast<const uint32_t*>(mrow + j0) : 0u;
+    uint32_t bits = 0;
+#pragma unroll
+    for (int c = 0; c < kListCols; ++c) bits |= (j0 + c < nb && ((w >> (8 * c)) & 0xffu) != 0u) ? (1u << c) : 0u;
+    cnt = __popc(bits);
+    return bits;
+  };
+  int count = 0;
+  for (int col = 0; col < nb; col += kListCols * NT) {
+    int cnt, tot;
+    selected(col + kListCols * t, cnt);
+    block_prefix4<NW>(cnt, lane, wave, sWaveCnt, tot);
+    count += tot;
+  }
+  const int target = count / 2;
+  if (t == 0) *sOut = 0;
+  int base = 0;
+  for (int col = 0; col < nb && base <= target; col += kListCols * NT) {
+    const int j0 = col + kListCols * t;
+    int cnt, tot;
+    uint32_t bits = selected(j0, cnt);
+    const int off = base + block_prefix4<NW>(cnt, lane, wave, sWaveCnt, tot);
+    if (target >= off && target < off + cnt) {
+      for (int r = target - off; r > 0; --r) bits &= bits - 1;  // drop the lower selected columns
+      *sOut = j0 + __builtin_ctz(bits);
+    }
+    base += tot;
+  }
+  __syncthreads();
+  const int J = *sOut;
+  __syncthreads();
+  return J;
+}
+
 template <int D, int B>
 __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) void bsa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint8_t* __restrict__ mask, int64_t pitch,
@@ -280,6 +344,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   __shared__ __align__(1024) unsigned char sV1[D * T::VROW];
   __shared__ int sList[T::LIST];
   __shared__ int sWaveCnt[T::NW];
+  __shared__ int sAnchor, sRot;
 
   const int wid = xcd_chunked<kXcdChunk>(blockIdx.x);
   if (wid >= n_heads * Lq) return;  // padding of the grid to whole chunk rounds
@@ -319,6 +384,18 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   bf16x8 pfp[2];  // d = 64 schedule: probabilities of the unit whose P V product is still pending
 
   const uint8_t* mrow = mask + ((int64_t)h * Lq + k) * pitch;
+  // Order of the stages (b = 128).  Neighbouring query blocks select mostly the same key blocks, each row's
+  // set shifted by about one block from the previous row's.  In ascending j a row then reads a shared block
+  // one block step after its neighbour, and 64 workgroups per XCD stream 4 MB in a block step, the size of
+  // the XCD's L2.  Every row therefore starts its (single-pass) list at a common column and wraps around:
+  // the median selected column of the first row of its group of 16 local query blocks, whose items the
+  // XCD dealing keeps together.  Neighbours then read their shared blocks at about the same time.  (An LRU
+  // model of one XCD's L2 under this dispatch puts the stage copies that hit in L2 at 65 % instead of 50 %
+  // at the HunyuanVideo shape, 57 % instead of 49 % at the Wan shape; at b = 64 ascending order is better.)
+  int anchor = 0;
+  if constexpr (B == 128)
+    anchor = median_column<T::NT, T::NW>(mask + ((int64_t)h * Lq + (k & ~15)) * pitch, nb, t, lane, wave, sWaveCnt,
+                                         &sAnchor);
   const int32_t* sof = slot_of + (int64_t)h * nb;
   const int tail_valid = N - (nb - 1) * B;  // real keys in the last block, 1..B
   const char* pk = reinterpret_cast<const char*>(packed);
@@ -326,6 +403,8 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   int col = 0;
   int seen = 0;  // selected blocks in the slot range, over all passes
   while (col < nb) {
+    const bool first_pass = col == 0;
+    if (t == 0) sRot = 0;
     // List the selected blocks of the next columns (ascending j) as (slot << 1 | is_last_block).  A thread
     // reads kListCols consecutive mask bytes with one load (rows are 16-byte aligned and their pitch is a
     // multiple of 16, so the word stays inside the row; columns >= nb are ignored) and looks up their slots;
@@ -365,9 +444,14 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         off += w < wave ? c : 0;
         add += c;
       }
+      int before_anchor = 0;
 #pragma unroll
       for (int c = 0; c < kListCols; ++c)
-        if (slots[c] >= 0) sList[off++] = (slots[c] << 1) | (j0 + c == nb - 1 ? 1 : 0);
+        if (slots[c] >= 0) {
+          sList[off++] = (slots[c] << 1) | (j0 + c == nb - 1 ? 1 : 0);
+          before_anchor += j0 + c < anchor ? 1 : 0;
+        }
+      if (before_anchor != 0) atomicAdd(&sRot, before_anchor);
       total += add;
       col += kListCols * T::NT;
       __syncthreads();
@@ -375,9 +459,15 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 
     seen += total;
     const int n = total * T::NST;  // stages of this pass
+    // Entries before the anchor go last (a row listed in one pass only).
+    const int rot = first_pass && col >= nb ? sRot : 0;
     if (n > 0) {
       // Slot code of stage s (clamped to the last stage: codes past the end are only read, never used).
-      auto code_of = [&](int s) { return __builtin_amdgcn_readfirstlane(sList[min(s, n - 1) / T::NST]); };
+      auto code_of = [&](int s) {
+        int e = min(s, n - 1) / T::NST + rot;
+        e -= e >= total ? total : 0;
+        return __builtin_amdgcn_readfirstlane(sList[e]);
+      };
       auto slot_ptr = [&](int code) { return pk + (int64_t)(code >> 1) * T::SLOT_BYTES; };
       // Offset of the first padding key inside unit g of stage s, counted from 8 half (>= 32: none).
       auto lim_of = [&](int code, int s, int g) {
