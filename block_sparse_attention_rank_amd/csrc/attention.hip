@@ -14,12 +14,12 @@
 // index swapped) so that each lane's eight probabilities of a 16-key MFMA step are eight consecutive
 // keys: every V^T fragment is then one 16-byte LDS read.
 //
-// Pipeline.  Every selected key block is consumed in stages of 64 keys.  A stage (64 K rows and the
-// matching 64 columns of V^T, 2 x 64 x d bf16) is copied from global memory straight into LDS with
-// global_load_lds_dwordx4 (no register staging); the next stage's copy is issued before the current one
-// is computed, into the other of two LDS buffers, and two workgroups share a CU.  The work is cut into
-// units of 32 keys.  At d = 128 a unit issues the next unit's score MFMAs beside its own softmax and then
-// its P V product, with two barriers per stage.  At d = 64, where the softmax costs twice as much per MFMA
+// Pipeline.  Every selected key block is consumed in stages of 64 keys (32 at d = 128, b = 64; see
+// stage_keys).  A stage (its K rows and the matching columns of V^T) is copied from global memory straight
+// into LDS with global_load_lds_dwordx4 (no register staging); the next stage's copy is issued before the
+// current one is computed, into the other of two LDS buffers, and two or more workgroups share a CU.  The
+// work is cut into units of 32 keys.  At d = 128 a unit issues the next unit's score MFMAs beside its own
+// softmax and then its P V product, with two barriers per 64-key stage (one per 32-key stage).  At d = 64, where the softmax costs twice as much per MFMA
 // flop, each unit's P V product is delayed to the next unit so that both products' MFMAs sit beside the
 // softmax arithmetic in one stretch of code, with one barrier per stage (measured: 5-11 % faster at d = 64,
 // 5 % slower at d = 128, where it needs all 256 VGPRs).  LDS rows are
@@ -70,7 +70,10 @@ __device__ __forceinline__ float sum_halves(float x) {
 // consecutive rows.
 template <int RowBytes>
 __device__ __forceinline__ int swizzle(int row) {
-  static_assert(RowBytes == 128 || RowBytes == 256, "row size");
+  // (64-byte rows, the V^T rows of a 32-key stage: four rows share the banks, so rows r, r + 4, r + 8 and
+  // r + 12 need distinct keys.)
+  static_assert(RowBytes == 64 || RowBytes == 128 || RowBytes == 256, "row size");
+  if constexpr (RowBytes == 64) return (row >> 2) & 3;  // four rows share the banks; rows r, r+4, r+8, r+12 apart
   return RowBytes == 256 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
 }
 
@@ -85,7 +88,15 @@ __device__ __forceinline__ void copy16(const char* base, uint32_t voff, const un
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(m0) : "memory");
 }
 
-constexpr int kStageKeys = 64;     // keys per pipeline stage
+// Keys per pipeline stage: 64, or 32 at d = 128, b = 64.  That shape's workgroup has two waves; with 64-key
+// double buffers of K and V^T (64 KiB) only two workgroups fit a CU, one wave per SIMD, and the compiler then
+// spends 292 registers a wave.  With 32-key stages (32 KiB) four fit, two waves per SIMD, in 197 registers:
+// measured 17 % faster on a HunyuanVideo-shaped share with 64-token blocks.  At d = 64, b = 64 the same change
+// (three waves per SIMD) was 11 % slower, and d = 128, b = 128 already holds two waves per SIMD.
+template <int D, int B>
+constexpr int stage_keys() {
+  return (D == 128 && B == 64) ? 32 : 64;
+}
 constexpr int kXcdChunk = 16;      // consecutive (head, query block) items kept on one XCD
 constexpr int kListCols = 4;       // mask columns a thread reads per listing step (one 32-bit load)
 
@@ -93,12 +104,13 @@ template <int D, int B>
 struct Tile {
   static constexpr int NW = B / 32;                      // waves, 32 query rows each
   static constexpr int NT = NW * 64;                     // threads
-  static constexpr int NST = B / kStageKeys;             // stages per key block
+  static constexpr int SK = stage_keys<D, B>();          // keys per stage
+  static constexpr int NST = B / SK;                     // stages per key block
   static constexpr int KROW = D * 2;                     // bytes per K row of a stage
-  static constexpr int KBYTES = kStageKeys * KROW;       // K part of a stage buffer
-  static constexpr int VROW = kStageKeys * 2;            // bytes per V^T row of a stage (128)
+  static constexpr int KBYTES = SK * KROW;               // K part of a stage buffer
+  static constexpr int VROW = SK * 2;                    // bytes per V^T row of a stage (128 or 64)
   static constexpr int STAGE = KBYTES + D * VROW;        // one stage buffer
-  static constexpr int CH = kStageKeys * D / 8;          // 16-byte chunks of K (and of V^T) per stage
+  static constexpr int CH = SK * D / 8;                  // 16-byte chunks of K (and of V^T) per stage
   static constexpr int CPT = CH / NT;                    // K (and V^T) chunks per thread per stage
   static constexpr int NDT = D / 32;                     // 32-row tiles of O^T
   static constexpr int NQF = D / 16;                     // Q fragments along d
@@ -129,7 +141,7 @@ struct CopyPlan {
       const int key = (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
       koff[i] = (uint32_t)(key * (D * 2) + c * 16);
       // V^T: LDS row e (a d index), chunk position cp holds keys 8 * (cp ^ swizzle(e)) .. +7.
-      const int e = q / 8, vp = q % 8;
+      const int e = q / (T::SK / 8), vp = q % (T::SK / 8);
       const int vc = vp ^ swizzle<T::VROW>(e);
       voff[i] = (uint32_t)(B * D * 2 + e * (B * 2) + vc * 16);
     }
@@ -366,7 +378,8 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
 #pragma unroll
   for (int f = 0; f < T::NQF; ++f) kread[f] = qr * T::KROW + (((2 * f + half) ^ swizzle<T::KROW>(qr)) * 16);
 #pragma unroll
-  for (int a = 0; a < 4; ++a) vread[a] = qr * T::VROW + (((2 * a + half) ^ swizzle<T::VROW>(qr)) * 16);
+  for (int a = 0; a < 4; ++a)  // 16-key steps of a stage: 4 at 64 keys, 2 at 32 (the rest unused)
+    vread[a] = a < T::SK / 16 ? qr * T::VROW + (((2 * a + half) ^ swizzle<T::VROW>(qr)) * 16) : 0u;
   CopyPlan<D, B> plan;
   plan.init(wave, lane);
 
@@ -471,10 +484,102 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
       auto slot_ptr = [&](int code) { return pk + (int64_t)(code >> 1) * T::SLOT_BYTES; };
       // Offset of the first padding key inside unit g of stage s, counted from 8 half (>= 32: none).
       auto lim_of = [&](int code, int s, int g) {
-        return (code & 1) ? tail_valid - (s % T::NST) * kStageKeys - 32 * g - 8 * half : 32;
+        return (code & 1) ? tail_valid - (s % T::NST) * T::SK - 32 * g - 8 * half : 32;
       };
 
-      if constexpr (D == 64) {
+      if constexpr (T::SK == 32 && D == 64) {
+        // 32-key stages, one unit each, P V product delayed by one unit.  At the top of unit s every lane waits for
+        // its copies of K[s + 1] and V^T[s - 1] (issued at the top of unit s - 1) and the workgroup meets, which
+        // frees K[s]'s buffer (last read by the lookahead scores of unit s - 1) and V^T[s - 2]'s (last read by
+        // the pending product of unit s - 1); K[s + 2] and V^T[s] are issued into them.
+        auto unit = [&](f32x16& cur, f32x16& nxt, const unsigned char* kbuf_next, const unsigned char* vbuf_prev,
+                        int lim) {
+          bf16x8 pf[2];
+          unit_mask(cur, lim);
+          nxt = unit_scores<D, B>(kbuf_next, 0, kread, qf);
+          float lu = unit_probabilities(cur, scale_log2, rs.m_run, pf);
+          unit_accumulate<D, B>(vbuf_prev, 0, vread, pfp, rs.oacc);
+          if (__builtin_amdgcn_ballot_w64(!(lu < 0x1p64f)) != 0) unit_rescale<D, B>(cur, rs, scale_log2, pf, lu);
+          rs.l_run += lu;
+          pfp[0] = pf[0];
+          pfp[1] = pf[1];
+        };
+        int c0 = code_of(0), c1 = code_of(1), c2 = code_of(2);  // codes of stages s, s + 1, s + 2
+        pfp[0] = bf16x8{};
+        pfp[1] = bf16x8{};
+        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the Q loads, see the 64-key schedule
+        plan.issue_k(slot_ptr(c0), 0, sK0, wave);
+        if (n > 1) {
+          plan.issue_k(slot_ptr(c1), 1 % T::NST, sK1, wave);
+          block_sync<T::CPT>();
+        } else {
+          block_sync<0>();
+        }
+        f32x16 sa = unit_scores<D, B>(sK0, 0, kread, qf), sb;
+        for (int s = 0; s < n; s += 2) {
+          block_sync<0>();
+          if (s + 2 < n) plan.issue_k(slot_ptr(c2), (s + 2) % T::NST, sK0, wave);
+          plan.issue_v(slot_ptr(c0), s % T::NST, sV0, wave);
+          int c3 = code_of(s + 3);
+          unit(sa, sb, sK1, sV1, lim_of(c0, s, 0));
+          if (s + 1 >= n) {
+            block_sync<0>();
+            unit_accumulate<D, B>(sV0, 0, vread, pfp, rs.oacc);
+            break;
+          }
+          c0 = c1; c1 = c2; c2 = c3;
+          block_sync<0>();
+          if (s + 3 < n) plan.issue_k(slot_ptr(c2), (s + 3) % T::NST, sK1, wave);
+          plan.issue_v(slot_ptr(c0), (s + 1) % T::NST, sV1, wave);
+          c3 = code_of(s + 4);
+          unit(sb, sa, sK0, sV0, lim_of(c0, s + 1, 0));
+          if (s + 2 >= n) {
+            block_sync<0>();
+            unit_accumulate<D, B>(sV1, 0, vread, pfp, rs.oacc);
+            break;
+          }
+          c0 = c1; c1 = c2; c2 = c3;
+        }
+      } else if constexpr (T::SK == 32) {
+        // 32-key stages, one unit each, P V product at once.  At the top of unit s every lane waits for its copies
+        // of K[s + 1] and V^T[s] (issued at the top of unit s - 1) and the workgroup meets, which frees K[s]'s
+        // buffer (last read by the lookahead scores of unit s - 1) and V^T[s - 1]'s; K[s + 2] and V^T[s + 1] are
+        // issued into them.
+        auto unit = [&](f32x16& cur, f32x16& nxt, const unsigned char* kbuf_next, const unsigned char* vbuf, int lim) {
+          bf16x8 pf[2];
+          unit_mask(cur, lim);
+          nxt = unit_scores<D, B>(kbuf_next, 0, kread, qf);
+          unit_softmax<D, B>(cur, rs, scale_log2, pf);
+          __builtin_amdgcn_s_setprio(1);
+          unit_accumulate<D, B>(vbuf, 0, vread, pf, rs.oacc);
+          __builtin_amdgcn_s_setprio(0);
+        };
+        int c0 = code_of(0), c1 = code_of(1), c2 = code_of(2);  // codes of stages s, s + 1, s + 2
+        plan.issue_k(slot_ptr(c0), 0, sK0, wave);
+        plan.issue_v(slot_ptr(c0), 0, sV0, wave);
+        if (n > 1) {
+          plan.issue_k(slot_ptr(c1), 1 % T::NST, sK1, wave);
+          block_sync<T::CPT>();
+        } else {
+          block_sync<0>();
+        }
+        f32x16 sa = unit_scores<D, B>(sK0, 0, kread, qf), sb;
+        for (int s = 0; s < n; s += 2) {
+          block_sync<0>();
+          if (s + 2 < n) plan.issue_k(slot_ptr(c2), (s + 2) % T::NST, sK0, wave);
+          if (s + 1 < n) plan.issue_v(slot_ptr(c1), (s + 1) % T::NST, sV1, wave);
+          int c3 = code_of(s + 3);
+          unit(sa, sb, sK1, sV0, lim_of(c0, s, 0));
+          if (s + 1 >= n) break;
+          c0 = c1; c1 = c2; c2 = c3;
+          block_sync<0>();
+          if (s + 3 < n) plan.issue_k(slot_ptr(c2), (s + 3) % T::NST, sK1, wave);
+          if (s + 2 < n) plan.issue_v(slot_ptr(c1), (s + 2) % T::NST, sV0, wave);
+          c3 = code_of(s + 4);
+          unit(sb, sa, sK0, sV1, lim_of(c0, s + 1, 0));
+          c0 = c1; c1 = c2; c2 = c3;
+        }
+      } else if constexpr (D == 64) {
         // One unit u: the scores of unit u + 1, the probabilities of unit u and the P V product of unit u - 1
         // (whose probabilities are already in pfp) are issued together, so the MFMAs of both products sit
         // beside the softmax arithmetic in one stretch of code; the rare rescale follows.  After the last unit

@@ -8,6 +8,7 @@ item by item on the host's cores (tests/_gpu.py).  The local set Q_r comes from 
 (sparsp_local_query_blocks) and must equal the generator's.
 """
 import math
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -108,6 +109,10 @@ EDGE_CASES = {
                                 k_offset_sigma=4.0),
     "multipass_d64_b128": custom(H=1, d=64, b=128, T=1, HW=128 * 1100 - 37, G=32, r=3, density=0.3),
     "multipass_d128_b64": custom(H=1, d=128, b=64, T=1, HW=64 * 1200, G=32, r=20, density=0.6),
+    # full-size shares in the two mixed (d, b) shapes: the HunyuanVideo-shaped share with 64-token blocks
+    # (d = 128, b = 64: the 32-key stage pipeline) and the LTX-Video-shaped share with 128-token blocks
+    "hunyuan_b64": replace(CONFIGS["hunyuan"], name="hunyuan_b64", b=64),
+    "ltx_b128": replace(CONFIGS["ltx"], name="ltx_b128", b=128),
 }
 
 
