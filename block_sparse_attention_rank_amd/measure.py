@@ -37,7 +37,8 @@ def _runs_beside(lib, khz: int, main, side) -> bool:
 
 
 def side_stream(main=None):
-    """A stream whose work runs concurrently with ``main`` (the current stream by default)."""
+    """A stream whose work runs concurrently with ``main`` (the current stream by default), or None when no
+    stream does (a profiler that serialises kernels, for one)."""
     import torch
     main = main if main is not None else torch.cuda.current_stream()
     key = main.cuda_stream
@@ -45,13 +46,12 @@ def side_stream(main=None):
         lib = load()
         khz = ctypes.c_int32(0)
         check(lib.sparsp_wall_clock_khz(ctypes.byref(khz)))
+        _SIDE[key] = None
         for _ in range(16):
             cand = torch.cuda.Stream()             # default priority
             if _runs_beside(lib, khz.value, main, cand):
                 _SIDE[key] = cand
                 break
-        else:
-            raise RuntimeError("no stream was found that runs beside the measured stream")
     return _SIDE[key]
 
 
@@ -63,7 +63,8 @@ class ClockWindow:
         ghz = cw.result()["ghz"]
 
     The sampler takes a sample every ``interval_us`` microseconds for at most ``max_seconds`` and then exits by
-    itself; the window must end before it does (result() reports how many samples fell inside)."""
+    itself; the window must end before it does (result() reports how many samples fell inside).  Where no
+    stream runs beside the measured one, nothing is sampled and the clock is reported as None."""
 
     def __init__(self, max_seconds: float = 0.5, interval_us: float = 20.0):
         import torch
@@ -83,6 +84,8 @@ class ClockWindow:
         import torch
         s = stream if stream is not None else torch.cuda.current_stream()
         side = side_stream(s)
+        if side is None:
+            return
         side.wait_stream(s)                        # the sampler starts after the work queued so far
         check(self._lib.sparsp_clock_sampler(ctypes.c_void_p(self.samples.data_ptr()), self.n, self.interval,
                                              ctypes.c_void_p(side.cuda_stream)))
@@ -100,6 +103,8 @@ class ClockWindow:
         torch.cuda.synchronize()
         smp = self.samples.cpu().numpy().reshape(-1, 2)
         t0, t1 = (int(x) for x in self.ts.cpu().numpy())
+        if t0 == 0:                                # not started: no stream ran beside the measured one
+            return dict(samples_in_window=0, window_us=None, ghz=None)
         smp = smp[smp[:, 1] > 0]
         inside = smp[(smp[:, 1] >= t0) & (smp[:, 1] <= t1)]
         out = dict(samples_in_window=int(len(inside)), window_us=round((t1 - t0) / self.khz * 1e3, 1), ghz=None)
