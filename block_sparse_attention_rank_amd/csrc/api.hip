@@ -138,11 +138,11 @@ int32_t sparsp_pack_kv(const sparsp_geometry* geom, const uint16_t* K, const uin
 namespace {
 
 // Shared checks and launch of the attention entry points over the slot range [slot_lo, slot_hi) and the heads
-// [h_lo, h_hi) (all heads when h_hi < 0).
+// [h_lo, h_hi) (all heads when h_hi < 0); `anchored` for the single-pass call only.
 int32_t attention_call(const char* fn, const sparsp_geometry* geom, const uint16_t* Q, const uint8_t* mask,
                        int64_t mask_pitch, const int32_t* slot_of, const uint16_t* packed, int32_t slot_lo,
                        int32_t slot_hi, float softmax_scale, float* O, float* lse, void* stream, int accumulate = 0,
-                       int32_t h_lo = 0, int32_t h_hi = -1) {
+                       int32_t h_lo = 0, int32_t h_hi = -1, int anchored = 0) {
   sparsp::Dims d;
   int32_t st = check_geometry(geom, fn, &d);
   if (st) return st;
@@ -155,7 +155,8 @@ int32_t attention_call(const char* fn, const sparsp_geometry* geom, const uint16
   if ((Q && !aligned16(Q)) || (packed && !aligned16(packed)) || (O && !aligned16(O)))
     return fail(SPARSP_ERR_INVALID, fn, "Q, packed and O must be 16-byte aligned");
   return hip_status(sparsp::launch_attention(d, Q, mask, mask_pitch, slot_of, packed, slot_lo, slot_hi, h_lo, h_hi,
-                                             softmax_scale, O, lse, accumulate, reinterpret_cast<hipStream_t>(stream)),
+                                             softmax_scale, O, lse, accumulate, anchored,
+                                             reinterpret_cast<hipStream_t>(stream)),
                     fn);
 }
 
@@ -167,7 +168,7 @@ int32_t sparsp_block_sparse_attn(const sparsp_geometry* geom, const uint16_t* Q,
   static const char* fn = "sparsp_block_sparse_attn";
   if (slot_capacity < 0) return fail(SPARSP_ERR_INVALID, fn, "slot_capacity must be >= 0");
   return attention_call(fn, geom, Q, mask, mask_pitch, slot_of, packed, 0, slot_capacity, softmax_scale, O, lse,
-                        stream);
+                        stream, 0, 0, -1, 1);
 }
 
 int32_t sparsp_block_sparse_attn_segment(const sparsp_geometry* geom, const uint16_t* Q, const uint8_t* mask,

@@ -345,7 +345,8 @@ template <int D, int B>
 __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) void bsa_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint8_t* __restrict__ mask, int64_t pitch,
     const int32_t* __restrict__ slot_of, const uint16_t* __restrict__ packed, int slot_lo, int slot_hi, float scale_log2,
-    int h_lo, int n_heads, int Lq, int nb, int N, float* __restrict__ O, float* __restrict__ lse, int accumulate) {
+    int h_lo, int n_heads, int Lq, int nb, int N, float* __restrict__ O, float* __restrict__ lse, int accumulate,
+    int anchored) {
   using T = Tile<D, B>;
   // Separate double buffers for K and V^T.  The work is cut into units of 32 keys (two per stage); the
   // scores of unit u + 1 are computed while unit u is turned into probabilities, and then unit u is
@@ -405,10 +406,13 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
   // XCD dealing keeps together.  Neighbours then read their shared blocks at about the same time.  (An LRU
   // model of one XCD's L2 under this dispatch puts the stage copies that hit in L2 at 65 % instead of 50 %
   // at the HunyuanVideo shape, 57 % instead of 49 % at the Wan shape; at b = 64 ascending order is better.)
+  // Only the single-pass call orders its stages this way: a segment or chunk launch lists only its piece's
+  // few blocks per row, where the order gains little, and skips the anchor's two passes over a mask row.
   int anchor = 0;
   if constexpr (B == 128)
-    anchor = median_column<T::NT, T::NW>(mask + ((int64_t)h * Lq + (k & ~15)) * pitch, nb, t, lane, wave, sWaveCnt,
-                                         &sAnchor);
+    if (anchored)
+      anchor = median_column<T::NT, T::NW>(mask + ((int64_t)h * Lq + (k & ~15)) * pitch, nb, t, lane, wave,
+                                           sWaveCnt, &sAnchor);
   const int32_t* sof = slot_of + (int64_t)h * nb;
   const int tail_valid = N - (nb - 1) * B;  // real keys in the last block, 1..B
   const char* pk = reinterpret_cast<const char*>(packed);
@@ -740,7 +744,7 @@ template <int D, int B>
 hipError_t launch_attention_t(const Dims& g, const uint16_t* Q, const uint8_t* mask, int64_t pitch,
                               const int32_t* slot_of, const uint16_t* packed, int32_t slot_lo, int32_t slot_hi,
                               int h_lo, int h_hi, float softmax_scale, float* O, float* lse, int accumulate,
-                              hipStream_t stream) {
+                              int anchored, hipStream_t stream) {
   const int64_t items = (int64_t)(h_hi - h_lo) * g.Lq;
   if (items == 0) return hipSuccess;
   const float scale_log2 = softmax_scale * 1.4426950408889634f;
@@ -748,7 +752,7 @@ hipError_t launch_attention_t(const Dims& g, const uint16_t* Q, const uint8_t* m
   const int64_t grid = (items + round - 1) / round * round;
   hipLaunchKernelGGL((bsa_fwd_kernel<D, B>), dim3((unsigned)grid), dim3(2 * B), 0, stream, Q, mask, pitch,
                      slot_of, packed, slot_lo, slot_hi, scale_log2, h_lo, h_hi - h_lo, g.Lq, g.nb, g.N, O, lse,
-                     accumulate);
+                     accumulate, anchored);
   return hipGetLastError();
 }
 
@@ -757,18 +761,18 @@ hipError_t launch_attention_t(const Dims& g, const uint16_t* Q, const uint8_t* m
 hipError_t launch_attention(const Dims& g, const uint16_t* Q, const uint8_t* mask, int64_t pitch,
                             const int32_t* slot_of, const uint16_t* packed, int32_t slot_lo, int32_t slot_hi,
                             int32_t h_lo, int32_t h_hi, float softmax_scale, float* O, float* lse, int accumulate,
-                            hipStream_t stream) {
+                            int anchored, hipStream_t stream) {
   if (g.d == 128 && g.b == 128)
     return launch_attention_t<128, 128>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, h_lo, h_hi, softmax_scale,
-                                        O, lse, accumulate, stream);
+                                        O, lse, accumulate, anchored, stream);
   if (g.d == 64 && g.b == 64)
     return launch_attention_t<64, 64>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, h_lo, h_hi, softmax_scale,
-                                      O, lse, accumulate, stream);
+                                      O, lse, accumulate, anchored, stream);
   if (g.d == 128 && g.b == 64)
     return launch_attention_t<128, 64>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, h_lo, h_hi, softmax_scale,
-                                       O, lse, accumulate, stream);
+                                       O, lse, accumulate, anchored, stream);
   return launch_attention_t<64, 128>(g, Q, mask, pitch, slot_of, packed, slot_lo, slot_hi, h_lo, h_hi, softmax_scale,
-                                     O, lse, accumulate, stream);
+                                     O, lse, accumulate, anchored, stream);
 }
 
 }  // namespace sparsp

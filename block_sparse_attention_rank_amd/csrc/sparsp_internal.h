@@ -31,11 +31,12 @@ hipError_t launch_pack(const Dims& g, const uint16_t* K, const uint16_t* V, cons
                        uint16_t* packed, hipStream_t stream);
 // Attention of heads [h_lo, h_hi) over the selected blocks whose slot lies in [slot_lo, slot_hi); only those
 // heads' (head, query block) items are launched.  accumulate = 0 writes (O, lse); 1 folds the result into the
-// running (O, lse) by their log-sum-exp (rows without keys in range untouched).
+// running (O, lse) by their log-sum-exp (rows without keys in range untouched).  anchored = 1 (the single-pass
+// call) walks each row's blocks from the anchor column of its group of query blocks instead of from the first.
 hipError_t launch_attention(const Dims& g, const uint16_t* Q, const uint8_t* mask, int64_t pitch,
                             const int32_t* slot_of, const uint16_t* packed, int32_t slot_lo, int32_t slot_hi,
                             int32_t h_lo, int32_t h_hi, float softmax_scale, float* O, float* lse, int accumulate,
-                            hipStream_t stream);
+                            int anchored, hipStream_t stream);
 // Fold a partial (O_part, lse_part) into (O, lse), rows of d floats.
 hipError_t launch_merge(int64_t rows, int d, float* O, float* lse, const float* O_part, const float* lse_part,
                         hipStream_t stream);
