@@ -3,7 +3,8 @@
 // are placed in the attention kernel's layout).  Slot s = (h, j) receives the K block token-major
 // (b x d) followed by the V block transposed (d x b), so the attention kernel's P V product reads
 // key-contiguous V rows.  The copy is HBM-bound: every byte is read once and written once with 16-byte
-// vector accesses; the V transpose happens in registers on 8 x 8 sub-tiles, so no LDS is involved.
+// vector accesses; the V transpose happens in registers on 8 x 8 sub-tiles (the LDS the launch reserves is
+// never touched: it only limits how many workgroups a CU holds).
 #include "sparsp_internal.h"
 
 namespace sparsp {

@@ -161,7 +161,10 @@ int32_t sparsp_pack_kv(const sparsp_geometry* g, const uint16_t* K, const uint16
  *   O            [H][Lq*b][d] float32: softmax-weighted sum of V rows                  (written)
  *   lse          [H][Lq*b] float32: natural-log log-sum-exp of the scaled logits       (written)
  * For local block k of head h the keys are the real tokens (index < N) of every block j with
- * mask[h][k][j] != 0, visited in ascending j; key tokens of the last block at index >= N are excluded.
+ * mask[h][k][j] != 0; key tokens of the last block at index >= N are excluded.  The blocks are visited in an
+ * order chosen for L2 locality (at b = 128 each row starts at a column shared with its neighbouring query
+ * blocks and wraps around); the result depends on the order only through rounding, and repeated calls on
+ * the same inputs give the same bits.
  * A row with no key gives O = 0 and lse = -inf.  A selected block whose slot_of entry is negative or
  * >= slot_capacity is skipped.  Inputs are bf16; products accumulate in fp32 and the softmax
  * probabilities are rounded to bf16 before the P V product.
