@@ -19,10 +19,11 @@
 // into LDS with global_load_lds_dwordx4 (no register staging); the next stage's copy is issued before the
 // current one is computed, into the other of two LDS buffers, and two or more workgroups share a CU.  The
 // work is cut into units of 32 keys.  At d = 128 a unit issues the next unit's score MFMAs beside its own
-// softmax and then its P V product, with two barriers per 64-key stage (one per 32-key stage).  At d = 64, where the softmax costs twice as much per MFMA
-// flop, each unit's P V product is delayed to the next unit so that both products' MFMAs sit beside the
-// softmax arithmetic in one stretch of code, with one barrier per stage (measured: 5-11 % faster at d = 64,
-// 5 % slower at d = 128, where it needs all 256 VGPRs).  LDS rows are
+// softmax and then its P V product, with two barriers per 64-key stage (one per 32-key stage).  At d = 64,
+// where the softmax costs twice as much per MFMA flop, each unit's P V product is delayed to the next unit
+// so that both products' MFMAs sit beside the softmax arithmetic in one stretch of code, with one barrier
+// per stage (measured: 5-11 % faster at d = 64, 5 % slower at d = 128, where it needs all 256 VGPRs).  LDS
+// rows are
 // XOR-swizzled in 16-byte chunks (chunk c of row m sits at c ^ swizzle(m)).  A 16-byte fragment read
 // is served 16 lanes at a time by 64 four-byte banks (256 bytes per clock), and its lanes read one
 // logical chunk of 16 consecutive rows, so the key gives those rows distinct bank groups; it also keeps
@@ -65,15 +66,14 @@ __device__ __forceinline__ float sum_halves(float x) {
 }
 
 // XOR key of the 16-byte chunks of an LDS row of `RowBytes` bytes (256: d = 128 K rows; 128: d = 64 K rows
-// and V^T rows).  A 256-byte row covers all 64 banks, so 16 consecutive rows need 16 distinct keys; two
-// 128-byte rows share the banks, so rows of equal parity among 16 need distinct keys, and so do 8
-// consecutive rows.
+// and the V^T rows of a 64-key stage; 64: the V^T rows of a 32-key stage).  A 256-byte row covers all 64
+// banks, so 16 consecutive rows need 16 distinct keys; two 128-byte rows share the banks, so rows of equal
+// parity among 16 need distinct keys, and so do 8 consecutive rows; four 64-byte rows share the banks, so
+// rows r, r + 4, r + 8 and r + 12 need distinct keys.
 template <int RowBytes>
 __device__ __forceinline__ int swizzle(int row) {
-  // (64-byte rows, the V^T rows of a 32-key stage: four rows share the banks, so rows r, r + 4, r + 8 and
-  // r + 12 need distinct keys.)
   static_assert(RowBytes == 64 || RowBytes == 128 || RowBytes == 256, "row size");
-  if constexpr (RowBytes == 64) return (row >> 2) & 3;  // four rows share the banks; rows r, r+4, r+8, r+12 apart
+  if constexpr (RowBytes == 64) return (row >> 2) & 3;
   return RowBytes == 256 ? (row & 15) : ((row & 7) ^ ((row >> 3) & 1));
 }
 
@@ -491,60 +491,7 @@ __global__ __launch_bounds__(2 * B) __attribute__((amdgpu_waves_per_eu(2, 2))) v
         return (code & 1) ? tail_valid - (s % T::NST) * T::SK - 32 * g - 8 * half : 32;
       };
 
-      if constexpr (T::SK == 32 && D == 64) {
-        // 32-key stages, one unit each, P V product delayed by one unit.  At the top of unit s every lane waits for
-        // its copies of K[s + 1] and V^T[s - 1] (issued at the top of unit s - 1) and the workgroup meets, which
-        // frees K[s]'s buffer (last read by the lookahead scores of unit s - 1) and V^T[s - 2]'s (last read by
-        // the pending product of unit s - 1); K[s + 2] and V^T[s] are issued into them.
-        auto unit = [&](f32x16& cur, f32x16& nxt, const unsigned char* kbuf_next, const unsigned char* vbuf_prev,
-                        int lim) {
-          bf16x8 pf[2];
-          unit_mask(cur, lim);
-          nxt = unit_scores<D, B>(kbuf_next, 0, kread, qf);
-          float lu = unit_probabilities(cur, scale_log2, rs.m_run, pf);
-          unit_accumulate<D, B>(vbuf_prev, 0, vread, pfp, rs.oacc);
-          if (__builtin_amdgcn_ballot_w64(!(lu < 0x1p64f)) != 0) unit_rescale<D, B>(cur, rs, scale_log2, pf, lu);
-          rs.l_run += lu;
-          pfp[0] = pf[0];
-          pfp[1] = pf[1];
-        };
-        int c0 = code_of(0), c1 = code_of(1), c2 = code_of(2);  // codes of stages s, s + 1, s + 2
-        pfp[0] = bf16x8{};
-        pfp[1] = bf16x8{};
-        __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): the Q loads, see the 64-key schedule
-        plan.issue_k(slot_ptr(c0), 0, sK0, wave);
-        if (n > 1) {
-          plan.issue_k(slot_ptr(c1), 1 % T::NST, sK1, wave);
-          block_sync<T::CPT>();
-        } else {
-          block_sync<0>();
-        }
-        f32x16 sa = unit_scores<D, B>(sK0, 0, kread, qf), sb;
-        for (int s = 0; s < n; s += 2) {
-          block_sync<0>();
-          if (s + 2 < n) plan.issue_k(slot_ptr(c2), (s + 2) % T::NST, sK0, wave);
-          plan.issue_v(slot_ptr(c0), s % T::NST, sV0, wave);
-          int c3 = code_of(s + 3);
-          unit(sa, sb, sK1, sV1, lim_of(c0, s, 0));
-          if (s + 1 >= n) {
-            block_sync<0>();
-            unit_accumulate<D, B>(sV0, 0, vread, pfp, rs.oacc);
-            break;
-          }
-          c0 = c1; c1 = c2; c2 = c3;
-          block_sync<0>();
-          if (s + 3 < n) plan.issue_k(slot_ptr(c2), (s + 3) % T::NST, sK1, wave);
-          plan.issue_v(slot_ptr(c0), (s + 1) % T::NST, sV1, wave);
-          c3 = code_of(s + 4);
-          unit(sb, sa, sK0, sV0, lim_of(c0, s + 1, 0));
-          if (s + 2 >= n) {
-            block_sync<0>();
-            unit_accumulate<D, B>(sV1, 0, vread, pfp, rs.oacc);
-            break;
-          }
-          c0 = c1; c1 = c2; c2 = c3;
-        }
-      } else if constexpr (T::SK == 32) {
+      if constexpr (T::SK == 32) {
         // 32-key stages, one unit each, P V product at once.  At the top of unit s every lane waits for its copies
         // of K[s + 1] and V^T[s] (issued at the top of unit s - 1) and the workgroup meets, which frees K[s]'s
         // buffer (last read by the lookahead scores of unit s - 1) and V^T[s - 1]'s; K[s + 2] and V^T[s + 1] are
