@@ -39,3 +39,16 @@ def test_clock_windows_on_several_streams(require_gpu):
         print(f"[measure] stream {i}: {r}", flush=True)
         assert r["samples_in_window"] >= 10, r
         assert 0.3 < r["ghz"] < 3.5, r
+
+
+def test_clock_window_without_a_concurrent_stream(require_gpu, monkeypatch):
+    """Where no stream runs beside the measured one (a profiler serialising kernels), a window samples
+    nothing and reports no clock instead of failing."""
+    import torch
+    from block_sparse_attention_rank_amd import measure
+    monkeypatch.setattr(measure, "_runs_beside", lambda *args: False)
+    monkeypatch.setattr(measure, "_SIDE", {})
+    s = torch.cuda.Stream()
+    r = _window(s)
+    print(f"[measure] serialised: {r}", flush=True)
+    assert r == {"samples_in_window": 0, "window_us": None, "ghz": None}
