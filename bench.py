@@ -593,57 +593,57 @@ def measure(sh: Share, steps: int, warmup: int, full: bool, args):
         print(f"[bench] {w.name}: chunk sweep " + ", ".join(f"{s['chunks']} chunks {s['fold_ms']:.3f} ms"
                                                               for s in sweep), file=sys.stderr, flush=True)
 
-        # Placement permutation (section 4.3) of the layer's hidden states [nb*b][H*d] bf16 into rank-major
-        # block order and back: each call reads and writes every byte once.
-        pos, _ = bsa.placement_permutation(sh.inp["placement"], g.G)
-        pos_d = torch.from_numpy(pos).cuda()
-        hidden = torch.randn((g.nb * g.b, g.H * g.d), device="cuda").to(torch.bfloat16)
-        hidden_p = torch.empty_like(hidden)
-        hidden_r = torch.empty_like(hidden)
-        for _ in range(2):
-            bsa.permute_blocks(hidden, pos_d, g.b, out=hidden_p)
-            bsa.permute_blocks(hidden_p, pos_d, g.b, inverse=True, out=hidden_r)
-        pev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(max(3, steps // 2))]
-        for e in pev:
-            e[0].record(stream)
-            bsa.permute_blocks(hidden, pos_d, g.b, out=hidden_p)
-            e[1].record(stream)
-            bsa.permute_blocks(hidden_p, pos_d, g.b, inverse=True, out=hidden_r)
-            e[2].record(stream)
-        torch.cuda.synchronize()
-        assert torch.equal(hidden_r, hidden), "permutation round trip changed the hidden states"
-        t_perm, t_iperm = float(np.mean(_ms(pev, 0, 1))), float(np.mean(_ms(pev, 1, 2)))
-        perm_bytes = 2 * hidden.numel() * hidden.element_size()
-        del hidden, hidden_p, hidden_r
-        comp.update({"permute_hidden_bytes": perm_bytes, "permute_us": round(t_perm * 1e3, 2),
-                     "permute_GBps": round(perm_bytes / (t_perm * 1e-3) / 1e9, 1),
-                     "permute_inverse_us": round(t_iperm * 1e3, 2),
-                     "permute_inverse_GBps": round(perm_bytes / (t_iperm * 1e-3) / 1e9, 1)})
+    # Placement permutation (section 4.3), on every workload: the layer's hidden states [nb*b][H*d] bf16 into
+    # rank-major block order and back; each call reads and writes every byte once.
+    pos, _ = bsa.placement_permutation(sh.inp["placement"], g.G)
+    pos_d = torch.from_numpy(pos).cuda()
+    hidden = torch.randn((g.nb * g.b, g.H * g.d), device="cuda").to(torch.bfloat16)
+    hidden_p = torch.empty_like(hidden)
+    hidden_r = torch.empty_like(hidden)
+    for _ in range(2):
+        bsa.permute_blocks(hidden, pos_d, g.b, out=hidden_p)
+        bsa.permute_blocks(hidden_p, pos_d, g.b, inverse=True, out=hidden_r)
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(max(3, steps // 2))]
+    for e in pev:
+        e[0].record(stream)
+        bsa.permute_blocks(hidden, pos_d, g.b, out=hidden_p)
+        e[1].record(stream)
+        bsa.permute_blocks(hidden_p, pos_d, g.b, inverse=True, out=hidden_r)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    assert torch.equal(hidden_r, hidden), "permutation round trip changed the hidden states"
+    t_perm, t_iperm = float(np.mean(_ms(pev, 0, 1))), float(np.mean(_ms(pev, 1, 2)))
+    perm_bytes = 2 * hidden.numel() * hidden.element_size()
+    del hidden, hidden_p, hidden_r
+    comp.update({"permute_hidden_bytes": perm_bytes, "permute_us": round(t_perm * 1e3, 2),
+                 "permute_GBps": round(perm_bytes / (t_perm * 1e-3) / 1e9, 1),
+                 "permute_inverse_us": round(t_iperm * 1e3, 2),
+                 "permute_inverse_GBps": round(perm_bytes / (t_iperm * 1e-3) / 1e9, 1)})
 
-        # Mask materialisation from pooled tiles (section 4.2): pool K (every block) and the local Q blocks,
-        # then score and select every local row (Top-p 0.9 with a Top-k floor of 16 blocks).
-        if g.nb <= 16384:
-            ids_d = torch.from_numpy(sh.inp["q_blocks"]).cuda()
-            kp = bsa.pool_blocks(g, sh.K)
-            qp = bsa.pool_blocks(g, sh.Q, block_ids=ids_d)
-            mat_mask = bsa.materialize_mask(g, qp, kp, 0.9, 16)
-            mev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(max(3, steps // 2))]
-            for e in mev:
-                e[0].record(stream)
-                bsa.pool_blocks(g, sh.K, out=kp)
-                e[1].record(stream)
-                bsa.pool_blocks(g, sh.Q, block_ids=ids_d, out=qp)
-                e[2].record(stream)
-                bsa.materialize_mask(g, qp, kp, 0.9, 16, out=mat_mask)
-                e[3].record(stream)
-            torch.cuda.synchronize()
-            t_pk, t_pq, t_sel = (float(np.mean(_ms(mev, i, i + 1))) for i in range(3))
-            k_bytes = sh.K.numel() * 2 * w.N // (g.nb * g.b)          # real rows of K are read
-            out["mask_materialisation"] = {
-                "pool_k_us": round(t_pk * 1e3, 2), "pool_k_GBps": round(k_bytes / (t_pk * 1e-3) / 1e9, 1),
-                "pool_q_us": round(t_pq * 1e3, 2), "select_us": round(t_sel * 1e3, 2), "tau": 0.9, "k_min": 16,
-                "density": round(float(mat_mask[:, :, :g.nb].float().mean().item()), 4)}
-            del kp, qp, mat_mask
+    # Mask materialisation from pooled tiles (section 4.2): pool K (every block) and the local Q blocks,
+    # then score and select every local row (Top-p 0.9 with a Top-k floor of 16 blocks).
+    if g.nb <= 16384:
+        ids_d = torch.from_numpy(sh.inp["q_blocks"]).cuda()
+        kp = bsa.pool_blocks(g, sh.K)
+        qp = bsa.pool_blocks(g, sh.Q, block_ids=ids_d)
+        mat_mask = bsa.materialize_mask(g, qp, kp, 0.9, 16)
+        mev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(max(3, steps // 2))]
+        for e in mev:
+            e[0].record(stream)
+            bsa.pool_blocks(g, sh.K, out=kp)
+            e[1].record(stream)
+            bsa.pool_blocks(g, sh.Q, block_ids=ids_d, out=qp)
+            e[2].record(stream)
+            bsa.materialize_mask(g, qp, kp, 0.9, 16, out=mat_mask)
+            e[3].record(stream)
+        torch.cuda.synchronize()
+        t_pk, t_pq, t_sel = (float(np.mean(_ms(mev, i, i + 1))) for i in range(3))
+        k_bytes = sh.K.numel() * 2 * w.N // (g.nb * g.b)          # real rows of K are read
+        out["mask_materialisation"] = {
+            "pool_k_us": round(t_pk * 1e3, 2), "pool_k_GBps": round(k_bytes / (t_pk * 1e-3) / 1e9, 1),
+            "pool_q_us": round(t_pq * 1e3, 2), "select_us": round(t_sel * 1e3, 2), "tau": 0.9, "k_min": 16,
+            "density": round(float(mat_mask[:, :, :g.nb].float().mean().item()), 4)}
+        del kp, qp, mat_mask
 
     if not args.no_comm:
         t0 = time.perf_counter()
